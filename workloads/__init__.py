@@ -1,0 +1,17 @@
+"""Seeded synthetic workloads for the tree-verification step (inputs only).
+
+This package is the single source of inputs shared by the CPU oracle, the
+GPU parity tests and the benchmark.  It draws tensors, token trees and random
+coins; it computes nothing that the verification method computes (no
+attention, no logits, no acceptance, no cache moves).
+"""
+from .gen import (  # noqa: F401
+    WORKLOADS,
+    Workload,
+    attn_inputs,
+    draft_coins,
+    draft_tokens,
+    lmhead_inputs,
+    bf16_bits_from_f32,
+    BF16_QNAN,
+)
