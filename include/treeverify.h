@@ -1,0 +1,170 @@
+/*
+ * treeverify.h - C ABI of the tree-verification step of tree speculative
+ * decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: JetSpec GitHub README, section "JetSpec > Overview":
+ * a draft head proposes a token tree, the frozen target model verifies the
+ * whole tree in one forward pass under a tree-causal attention mask, and the
+ * accepted path is chosen from the target's own logits, so decoding stays
+ * lossless.  The README's "Quick Start" runs at temperature 0.  The
+ * EQSPEC/EXSPEC abstract (arXiv 2510.22876, on the RSS reader page) names
+ * output equivalence with plain autoregressive decoding as the correctness
+ * criterion and the per-sequence KV-cache state of a ragged batch.
+ *
+ * One step is four calls on one stream, in this order:
+ *   tv_tree_verify_attn -> tv_lmhead_argmax -> tv_tree_accept -> tv_kv_compact
+ *
+ * Conventions shared by every call
+ *   - Every array pointer is a DEVICE pointer owned by the caller; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls validate their arguments on the host, enqueue their kernels on
+ *     `stream` and return at once; results are ready when the stream is.
+ *   - Return value: TV_OK (0), or a negative TV_E* code.  On a negative
+ *     return nothing was enqueued, except TV_EHIP, whose text is available
+ *     from tv_status_string() of that code until the next call on the thread.
+ *   - dtype: TV_BF16 (bfloat16 storage, fp32 accumulation on MFMA) or TV_F32
+ *     (fp32 storage and arithmetic).
+ *   - dev_status (nullable): device int32[B] that the caller zeroes; kernels
+ *     OR TV_STATUS_* flags into entry b when sequence b is malformed; the
+ *     outputs of such a sequence are then unspecified.
+ *   - Calls that share a workspace, or that write the same cache, must not
+ *     overlap in time (same stream, or ordered by events).
+ */
+#ifndef TREEVERIFY_H
+#define TREEVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_OK          0
+#define TV_EINVAL     -1 /* bad shape, size or null pointer                  */
+#define TV_ENOTSUP    -2 /* valid but unsupported: head dim, dtype, N, ...   */
+#define TV_EWORKSPACE -3 /* workspace null or smaller than the query result  */
+#define TV_EHIP       -4 /* a HIP launch failed                              */
+
+#define TV_BF16 0
+#define TV_F32  1
+
+#define TV_STATUS_BAD_PARENT 1 /* parent[0] != -1 or parent[i] not in [0, i) */
+#define TV_STATUS_BAD_LEN    2 /* L_b < 0, L_b > max_seq_len or L_b+N > Lcap */
+#define TV_STATUS_DEPTH      4 /* accepted path longer than P                */
+
+#define TV_MAX_NODES 1024 /* N limit of every call                           */
+
+/*
+ * Tree-causal attention (JetSpec GitHub README, "JetSpec > Overview": the
+ * whole tree is verified in one pass under a tree-causal mask).
+ *
+ * For sequence b, node i (0 <= i < N) and query head h (KV head g = h / G,
+ * G = Hq / Hkv), with L = seq_lens[b]:
+ *   visible keys = cache rows 0..L-1 (the prefix) and rows L + j for every
+ *                  tree node j on the root-to-i path, i included;
+ *   out[b][i][h] = sum_t softmax_t(scale * q . k_t) v_t over those keys.
+ * Node 0 is the last accepted token; the tree is topologically ordered:
+ * parent[b][0] = -1 and 0 <= parent[b][i] < i.
+ *
+ * q        [B][N][Hq][D]         dtype
+ * k_cache  [B][Hkv][Lcap][D]     dtype; rows L..L+N-1 hold the tree nodes'
+ * v_cache  [B][Hkv][Lcap][D]     keys/values in node order (read only)
+ * seq_lens [B] int32             prefix length of each sequence
+ * parent   [B][N] int32
+ * out      [B][N][Hq][D]         dtype (written)
+ * max_seq_len   host-side upper bound of seq_lens (sizes the split of the
+ *               prefix across workgroups); needs max_seq_len + N <= Lcap
+ * scale         softmax scale, normally 1/sqrt(D)
+ * workspace     device scratch of at least tv_tree_verify_attn_workspace()
+ *               bytes for the same shapes (may be NULL when that is 0)
+ * Supported: D in {64, 128}, 1 <= N <= TV_MAX_NODES, Hq % Hkv == 0.
+ * Device-side checks: TV_STATUS_BAD_PARENT, TV_STATUS_BAD_LEN.
+ */
+size_t tv_tree_verify_attn_workspace(int B, int N, int Hq, int Hkv, int D,
+                                     int max_seq_len, int dtype);
+int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, const int32_t* parent,
+                        void* out, int B, int N, int Hq, int Hkv, int D,
+                        int Lcap, int max_seq_len, float scale, int dtype,
+                        void* workspace, size_t ws_bytes, int32_t* dev_status,
+                        void* stream);
+
+/*
+ * Target LM head fused with a per-row argmax (the accepted path follows the
+ * target's own logits; temperature 0 makes that the argmax).
+ *
+ *   logits[r][v] = sum_k hidden[r][k] * w[v][k]   (fp32 accumulation)
+ *   argmax[r]    = smallest v attaining max_v logits[r][v]
+ *
+ * hidden  [M][K] dtype, row r = b*N + i for node i of sequence b
+ * w       [V][K] dtype (one row per vocabulary entry)
+ * argmax  [M] int32 (written)
+ * logits  [M][V] fp32 or NULL; written only when non-NULL (for checking:
+ *         the step itself never materialises the logits)
+ * workspace  at least tv_lmhead_argmax_workspace() bytes.  It must be
+ *         zero-filled before its first use; every call leaves it zero-filled
+ *         again when its kernel completes, so one buffer serves any number of
+ *         calls in stream order.
+ * Supported: bf16 needs K % 128 == 0; M >= 1, V >= 1.
+ */
+size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype);
+int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
+                     float* logits, int M, int K, int V, int dtype,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Greedy longest-accepted-path selection plus the bonus token (JetSpec GitHub
+ * README, "JetSpec > Overview": lossless by construction).
+ *
+ * Node i >= 1 is accepted when its parent is accepted and
+ * draft_tokens[b][i] == target_tokens[b][parent[i]]; the root is always
+ * accepted.  best = deepest accepted node, smallest index on ties.
+ *   path[b][0..path_len-1] = root .. best (node indices), rest = -1
+ *   path_len[b]            = depth(best) + 1
+ *   bonus[b]               = target_tokens[b][best]
+ * Emitting draft_tokens[path[1..]] followed by bonus equals what greedy
+ * decoding with the same target tokens would emit.
+ *
+ * parent, draft_tokens, target_tokens  [B][N] int32
+ * path [B][P] int32, path_len [B] int32, bonus [B] int32 (written)
+ * Device-side checks: TV_STATUS_BAD_PARENT, TV_STATUS_DEPTH; a flagged
+ * sequence gets path_len 0, bonus -1 and path all -1.
+ * Supported: 1 <= N <= TV_MAX_NODES, 1 <= P <= 64.
+ */
+int tv_tree_accept(const int32_t* parent, const int32_t* draft_tokens,
+                   const int32_t* target_tokens, int32_t* path,
+                   int32_t* path_len, int32_t* bonus, int B, int N, int P,
+                   int32_t* dev_status, void* stream);
+
+/*
+ * KV compaction: commit the accepted path into contiguous cache rows
+ * (EQSPEC/EXSPEC abstract: each sequence of a ragged batch keeps its own KV
+ * state).  For every b, KV head and j < path_len[b]:
+ *   row L_b + j  <-  row L_b + path[b][j]     (in k_cache and v_cache)
+ * then seq_lens[b] += path_len[b].  Rows are moved as stored bits; the moves
+ * of one (b, head) are staged before any is written, so the in-place update
+ * is exact.  Rows past the new length keep unspecified contents.
+ *
+ * k_cache, v_cache [B][Hkv][Lcap][D] dtype (updated in place)
+ * seq_lens [B] int32 (updated in place); path [B][P], path_len [B] int32
+ * The caller guarantees L_b + path_len[b] <= Lcap and path entries in
+ * [0, Lcap - L_b); rows are not read past that.
+ * Supported: D * sizeof(dtype) % 16 == 0, P <= 64.
+ */
+int tv_kv_compact(void* k_cache, void* v_cache, int32_t* seq_lens,
+                  const int32_t* path, const int32_t* path_len, int B, int Hkv,
+                  int D, int Lcap, int P, int dtype, void* stream);
+
+/* Text of a status code (TV_EHIP: the HIP error text of the failed launch). */
+const char* tv_status_string(int status);
+
+/* Version of this ABI: major * 10000 + minor * 100 + patch. */
+int tv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREEVERIFY_H */

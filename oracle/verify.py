@@ -59,7 +59,7 @@ def ancestors(parent_row, i: int) -> list[int]:
 # step 1: tree-causal attention
 
 def tree_attention(q, k_cache, v_cache, seq_lens, parent, scale, dtype,
-                   node_chunk: int = 128) -> np.ndarray:
+                   node_chunk: int = 128, nodes=None) -> np.ndarray:
     """Output of every (sequence b, node i, query head h), in fp64.
 
     Definition (JetSpec GitHub README, "JetSpec > Overview": the whole tree
@@ -70,6 +70,8 @@ def tree_attention(q, k_cache, v_cache, seq_lens, parent, scale, dtype,
         o = sum_t softmax(s)_t v_t.
     Query head h reads KV head h // G.  The prefix scores of a chunk of nodes
     are one matmul; the softmax is taken over the union of both key sets.
+    ``nodes`` restricts the work to those node indices (in every sequence);
+    the other outputs are left as NaN.
     """
     Q = decode(q, dtype)
     K = decode(k_cache, dtype)
@@ -79,21 +81,23 @@ def tree_attention(q, k_cache, v_cache, seq_lens, parent, scale, dtype,
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
-    out = np.zeros((B, N, Hq, D), dtype=np.float64)
+    out = np.full((B, N, Hq, D), np.nan)
+    todo = np.arange(N) if nodes is None else np.unique(np.asarray(nodes, dtype=np.int64))
     for b in range(B):
         L = int(seq_lens[b])
-        anc = [np.array(ancestors(parent[b], i), dtype=np.int64) for i in range(N)]
+        anc = {int(i): np.array(ancestors(parent[b], int(i)), dtype=np.int64) for i in todo}
         for g in range(Hkv):
             Kp, Vp = K[b, g, :L], Vv[b, g, :L]
-            for n0 in range(0, N, node_chunk):
-                n1 = min(N, n0 + node_chunk)
-                Qc = Q[b, n0:n1, g * G:(g + 1) * G, :]          # [n, G, D]
+            for c0 in range(0, len(todo), node_chunk):
+                sel = todo[c0:c0 + node_chunk]
+                Qc = Q[b, sel, g * G:(g + 1) * G, :]            # [n, G, D]
                 s_pre = (Qc @ Kp.T) * scale                       # [n, G, L]
-                for i in range(n0, n1):
+                for n, i in enumerate(sel):
+                    i = int(i)
                     rows = L + anc[i]
                     Ka, Va = K[b, g, rows], Vv[b, g, rows]        # [a, D]
                     s_anc = (Q[b, i, g * G:(g + 1) * G] @ Ka.T) * scale  # [G, a]
-                    sp = s_pre[i - n0]
+                    sp = s_pre[n]
                     m = np.maximum(sp.max(axis=1) if L else -np.inf,
                                    s_anc.max(axis=1))[:, None]
                     p_pre = np.exp(sp - m)

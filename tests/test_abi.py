@@ -1,0 +1,126 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol,
+and rejects bad arguments on the host before touching the GPU.
+
+Only calls that fail host validation are made here (no GPU is needed); the
+library is built first if it is not there yet.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "treeverify.h")
+
+
+def _lib_path():
+    from tree_draft_verification_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from tree_draft_verification_amd.build import build
+        build()
+    return _lib.LIB_PATH
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tree_draft_verification_amd import _lib
+    return _lib.load(_lib_path())
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
+              "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
+              "tv_status_string", "tv_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (tv_\w+)", out))
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    from tree_draft_verification_amd import _lib
+    assert set(_lib.SIGNATURES) == set(_declared_functions())
+
+
+def test_status_strings_and_version(lib):
+    assert lib.tv_abi_version() == 10000
+    for code in (0, -1, -2, -3, -4):
+        assert lib.tv_status_string(code)
+    assert lib.tv_status_string(-99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, sl=FAKE, par=FAKE, out=FAKE, B=1, N=64, Hq=32, Hkv=8,
+             D=128, Lcap=2048, msl=1024, scale=0.088, dtype=0, ws=FAKE, wsb=1 << 30,
+             st=None, stream=None)
+    a.update(kw)
+    return lib.tv_tree_verify_attn(a["q"], a["k"], a["v"], a["sl"], a["par"], a["out"],
+                                   a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], a["Lcap"],
+                                   a["msl"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+                                   a["st"], a["stream"])
+
+
+def test_attention_host_validation(lib):
+    assert _attn(lib, q=None) == -1
+    assert _attn(lib, out=None) == -1
+    assert _attn(lib, Hq=30) == -1                       # Hq % Hkv
+    assert _attn(lib, msl=2000) == -1                    # max_seq_len + N > Lcap
+    assert _attn(lib, N=0) == -1
+    assert _attn(lib, scale=float("nan")) == -1
+    assert _attn(lib, D=96) == -2
+    assert _attn(lib, dtype=7) == -2
+    assert _attn(lib, N=1025, Lcap=4096) == -2
+    need = lib.tv_tree_verify_attn_workspace(1, 64, 32, 8, 128, 1024, 0)
+    assert need > 0                                      # the prefix is split
+    assert _attn(lib, ws=None) == -3
+    assert _attn(lib, wsb=need - 1) == -3
+    assert lib.tv_tree_verify_attn_workspace(4, 1024, 32, 4, 128, 4096, 0) == 0
+
+
+def test_lmhead_host_validation(lib):
+    ws = lib.tv_lmhead_argmax_workspace(64, 4096, 151936, 0)
+    assert ws >= 64 * 8
+    f = lib.tv_lmhead_argmax
+    assert f(None, FAKE, FAKE, None, 64, 4096, 151936, 0, FAKE, ws, None) == -1
+    assert f(FAKE, FAKE, None, None, 64, 4096, 151936, 0, FAKE, ws, None) == -1
+    assert f(FAKE, FAKE, FAKE, None, 0, 4096, 151936, 0, FAKE, ws, None) == -1
+    assert f(FAKE, FAKE, FAKE, None, 64, 4000, 151936, 0, FAKE, ws, None) == -2
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 5, FAKE, ws, None) == -2
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, None, ws, None) == -3
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, FAKE, ws - 1, None) == -3
+
+
+def test_accept_and_compact_host_validation(lib):
+    a = lib.tv_tree_accept
+    assert a(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 32, None, None) == -1
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 32, None, None) == -1
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2048, 32, None, None) == -2
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 64, 65, None, None) == -2
+    c = lib.tv_kv_compact
+    assert c(None, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 2048, 32, 0, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 2048, 0, 0, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2048, 32, 0, None) == -2   # 8-byte rows
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 2048, 32, 3, None) == -2
+
+
+def test_binding_names_match_the_c_calls():
+    import tree_draft_verification_amd as tv
+    for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
+              "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
+              "tv_status_string", "tv_abi_version"):
+        assert callable(getattr(tv, n))
+    assert tv.tv_status_string(-3) == "workspace missing or too small"

@@ -1,0 +1,336 @@
+"""GPU parity at sizes the oracle finishes in seconds: element by element.
+
+Every call goes through the C-ABI library (via the thin binding).  Inputs
+are the seeded workloads; expected values come from the fp64 oracle only.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs
+
+from _helpers import (LOGITS_REL_L2, assert_argmax_ok, assert_attn_close, i32_dev,
+                      to_dev, to_host_bits, to_host_f64)
+
+pytestmark = pytest.mark.gpu
+
+Q8 = WORKLOADS["qwen3_8b_L1024_N64"]
+A3B = WORKLOADS["qwen3_30b_a3b_B4_L4096_N1024"]
+
+# Small attention cases: several key tiles, ragged tails, GQA 1/3/4/8, D 64/128.
+ATTN_CASES = {
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "q8_L300_N64": Q8.replace(L_lo=300, L_hi=300, seed=11),
+    "q8_bfs_L1000_N256": WORKLOADS["qwen3_8b_L16384_N256"].replace(L_lo=1000, L_hi=1000, seed=12),
+    "q8_ragged3_N64": WORKLOADS["qwen3_8b_ragged8_N64"].replace(B=3, L_lo=100, L_hi=700, seed=13),
+    "a3b_B2_L257_N200": A3B.replace(B=2, L_lo=257, L_hi=257, N=200, seed=14),
+    "d64_bf16_L129_N33": Q8.replace(Hq=8, Hkv=2, D=64, L_lo=129, L_hi=129, N=33, seed=15),
+    "g3_L70_N50": Q8.replace(Hq=12, Hkv=4, L_lo=70, L_hi=70, N=50, seed=16),
+    "g1_L64_N130": Q8.replace(Hq=4, Hkv=4, L_lo=64, L_hi=64, N=130, seed=17),
+    "empty_prefix_N20": Q8.replace(L_lo=0, L_hi=0, N=20, seed=18),
+    "single_node_L77": Q8.replace(L_lo=77, L_hi=77, N=1, seed=19),
+    "f32_gqa_L90_N20": Q8.replace(dtype="f32", Hq=8, Hkv=2, L_lo=90, L_hi=90, N=20, seed=20),
+}
+
+
+def _run_attn(a, wl, parent=None, max_seq_len=None):
+    import tree_draft_verification_amd as tv
+    par = a["parent"] if parent is None else parent
+    q = to_dev(a["q"], wl.dtype)
+    k = to_dev(a["k_cache"], wl.dtype)
+    v = to_dev(a["v_cache"], wl.dtype)
+    out = tv.tv_tree_verify_attn(q, k, v, i32_dev(a["seq_lens"]), i32_dev(par),
+                                 max_seq_len=int(a["seq_lens"].max()) if max_seq_len is None
+                                 else max_seq_len, scale=a["scale"])
+    return out
+
+
+@pytest.mark.parametrize("name", list(ATTN_CASES))
+def test_attention_elementwise(name):
+    wl = ATTN_CASES[name]
+    a = attn_inputs(wl)
+    print(f"[attn] {name} B={wl.B} N={wl.N} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} "
+          f"L={list(a['seq_lens'])}", flush=True)
+    out = _run_attn(a, wl)
+    ref = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"],
+                                a["parent"], a["scale"], wl.dtype)
+    got = to_host_f64(out)
+    mx, rel = assert_attn_close(got, ref, name)
+    if wl.dtype == "f32":
+        assert mx < 1e-5, f"fp32 path should be near-exact, max|d|={mx}"
+
+
+@pytest.mark.parametrize("shape", ["chain", "star"])
+def test_attention_chain_and_star_trees(shape):
+    """Chain tree == causal attention and star tree (every node a root child)."""
+    wl = Q8.replace(L_lo=200, L_hi=200, N=100, seed=21)
+    a = attn_inputs(wl)
+    N = wl.N
+    if shape == "chain":
+        parent = np.arange(-1, N - 1, dtype=np.int32)[None]
+    else:
+        parent = np.zeros((1, N), np.int32)
+        parent[0, 0] = -1
+    out = _run_attn(a, wl, parent=parent)
+    ref = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"],
+                                parent, a["scale"], wl.dtype)
+    assert_attn_close(to_host_f64(out), ref, shape)
+
+
+def test_attention_deep_chain_1024_nodes():
+    wl = A3B.replace(B=1, Hq=8, Hkv=1, L_lo=40, L_hi=40, N=1024, seed=22)
+    a = attn_inputs(wl)
+    parent = np.arange(-1, 1023, dtype=np.int32)[None]
+    out = _run_attn(a, wl, parent=parent)
+    nodes = [0, 1, 63, 64, 65, 500, 1022, 1023]
+    ref = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"], parent,
+                                a["scale"], wl.dtype, nodes=nodes)
+    assert_attn_close(to_host_f64(out), ref, "chain1024")
+
+
+def test_attention_flags_bad_trees_and_lengths():
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = Q8.replace(B=2, L_lo=100, L_hi=100, N=16, seed=23)
+    a = attn_inputs(wl)
+    parent = a["parent"].copy()
+    parent[1, 5] = 9                                    # parent[i] >= i in sequence 1
+    st = torch.zeros(2, dtype=torch.int32, device="cuda")
+    q, k, v = (to_dev(a[x], "bf16") for x in ("q", "k_cache", "v_cache"))
+    tv.tv_tree_verify_attn(q, k, v, i32_dev(a["seq_lens"]), i32_dev(parent),
+                           max_seq_len=100, dev_status=st)
+    assert st.cpu().tolist() == [0, tv.TV_STATUS_BAD_PARENT]
+    st.zero_()
+    lens = a["seq_lens"].copy()
+    lens[0] = 101                                       # above max_seq_len
+    tv.tv_tree_verify_attn(q, k, v, i32_dev(lens), i32_dev(a["parent"]),
+                           max_seq_len=100, dev_status=st)
+    assert st.cpu().tolist() == [tv.TV_STATUS_BAD_LEN, 0]
+
+
+def test_attention_deterministic():
+    wl = ATTN_CASES["q8_bfs_L1000_N256"]
+    a = attn_inputs(wl)
+    o1 = to_host_bits(_run_attn(a, wl))
+    o2 = to_host_bits(_run_attn(a, wl))
+    np.testing.assert_array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------- LM head
+
+LM_CASES = {
+    "tiny_fp32": WORKLOADS["tiny_fp32"],
+    "M64_K4096_V8192": Q8.replace(V=8192, seed=31),
+    "M100_K256_V1001": Q8.replace(B=1, N=100, hidden=256, V=1001, seed=32),
+    "M1_K128_V130": Q8.replace(N=1, hidden=128, V=130, seed=33),
+    "M256_K512_V4163": Q8.replace(N=256, hidden=512, V=4163, seed=34),
+    "M513_K128_V2000": Q8.replace(B=1, N=513, hidden=128, V=2000, seed=35),
+    "f32_M40_K100_V777": Q8.replace(dtype="f32", N=40, hidden=100, V=777, seed=36),
+}
+
+
+@pytest.mark.parametrize("name", list(LM_CASES))
+def test_lmhead_elementwise(name):
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = LM_CASES[name]
+    lm = lmhead_inputs(wl)
+    M, V = wl.M, wl.V
+    print(f"[lmhead] {name} M={M} K={wl.hidden} V={V}", flush=True)
+    h = to_dev(lm["hidden"], wl.dtype)
+    w = to_dev(lm["w"], wl.dtype)
+    logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(tv.tv_lmhead_argmax_workspace(M, wl.hidden, V), dtype=torch.uint8,
+                     device="cuda")
+    arg = tv.tv_lmhead_argmax(h, w, logits=logits, workspace=ws)
+    got_l = logits.cpu().numpy().astype(np.float64)
+    ref_l = oracle.lm_logits(lm["hidden"], lm["w"], wl.dtype)
+    rel = np.linalg.norm(got_l - ref_l) / np.linalg.norm(ref_l)
+    assert rel <= LOGITS_REL_L2, f"logits rel L2 {rel:.3e}"
+    ref = oracle.lm_head_argmax(lm["hidden"], lm["w"], wl.dtype)
+    assert_argmax_ok(arg.cpu().numpy(), ref, name)
+    # the workspace is left zeroed, and a second call (no logits) agrees
+    assert int(ws.count_nonzero()) == 0
+    arg2 = tv.tv_lmhead_argmax(h, w, workspace=ws)
+    np.testing.assert_array_equal(arg2.cpu().numpy(), arg.cpu().numpy())
+
+
+def test_lmhead_ties_go_to_smallest_index():
+    import tree_draft_verification_amd as tv
+    from workloads import bf16_bits_from_f32
+    rng = np.random.default_rng(37)
+    M, K, V = 70, 256, 3000
+    Hi = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    Wi = rng.integers(-2, 3, size=(V, K)).astype(np.float32)
+    Wi[2500] = Wi[11]          # duplicate rows -> exact ties across workgroups
+    Wi[1234] = Wi[11]
+    Wi[129] = Wi[128]          # a tie inside one workgroup tile
+    h = bf16_bits_from_f32(Hi)
+    w = bf16_bits_from_f32(Wi)
+    exact = Hi.astype(np.int64) @ Wi.T.astype(np.int64)
+    arg = tv.tv_lmhead_argmax(to_dev(h, "bf16"), to_dev(w, "bf16")).cpu().numpy()
+    np.testing.assert_array_equal(arg, np.argmax(exact, axis=1))
+
+
+# ---------------------------------------------------------------- accept + compact
+
+def _accept_gpu(parent, draft, tgt, P):
+    import tree_draft_verification_amd as tv
+    path, plen, bonus = tv.tv_tree_accept(i32_dev(parent), i32_dev(draft), i32_dev(tgt), P)
+    return path.cpu().numpy(), plen.cpu().numpy(), bonus.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_accept_bit_exact_on_workload_trees(name):
+    wl = WORKLOADS[name]
+    small = wl.replace(L_lo=min(wl.L_lo, 64), L_hi=min(wl.L_hi, 64), Hq=1, Hkv=1, D=64)
+    a = attn_inputs(small)
+    rng = np.random.default_rng(41)
+    for trial in range(4):
+        tgt = rng.integers(0, 50, size=(wl.B, wl.N)).astype(np.int32)
+        draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"], seed=wl.seed + trial), tgt)
+        ref = oracle.tree_accept(a["parent"], draft, tgt, P=32)
+        path, plen, bonus = _accept_gpu(a["parent"], draft, tgt, 32)
+        np.testing.assert_array_equal(plen, ref["path_len"])
+        np.testing.assert_array_equal(path, ref["path"])
+        np.testing.assert_array_equal(bonus, ref["bonus"])
+
+
+def test_accept_exhaustive_small_trees():
+    import itertools
+    rng = np.random.default_rng(42)
+    parents, drafts, tgts = [], [], []
+    for choice in itertools.product(*[range(i) for i in range(1, 6)]):
+        parents.append([-1, *choice])
+        drafts.append(rng.integers(0, 2, size=6))
+        tgts.append(rng.integers(0, 2, size=6))
+    parent = np.array(parents, np.int32)
+    draft = np.array(drafts, np.int32)
+    tgt = np.array(tgts, np.int32)
+    ref = oracle.tree_accept(parent, draft, tgt, P=8)
+    path, plen, bonus = _accept_gpu(parent, draft, tgt, 8)
+    np.testing.assert_array_equal(path, ref["path"])
+    np.testing.assert_array_equal(plen, ref["path_len"])
+    np.testing.assert_array_equal(bonus, ref["bonus"])
+
+
+def test_accept_edge_cases_and_flags():
+    import torch
+    import tree_draft_verification_amd as tv
+    N = 40
+    chain = np.arange(-1, N - 1, dtype=np.int32)
+    tgt = np.arange(500, 500 + N, dtype=np.int32)
+    all_match = np.concatenate([[3], tgt[:-1]]).astype(np.int32)
+    no_match = np.full(N, 7, np.int32)
+    star = np.zeros(N, np.int32)
+    star[0] = -1
+    parent = np.stack([chain, chain, star, chain, chain])
+    draft = np.stack([all_match, no_match, np.full(N, 500, np.int32), all_match, all_match])
+    tgts = np.stack([tgt] * 5)
+    parent[3, 7] = 12                                   # malformed
+    st = torch.zeros(5, dtype=torch.int32, device="cuda")
+    path, plen, bonus = tv.tv_tree_accept(i32_dev(parent), i32_dev(draft), i32_dev(tgts), 48,
+                                          dev_status=st)
+    plen, bonus, path = plen.cpu().numpy(), bonus.cpu().numpy(), path.cpu().numpy()
+    assert plen[0] == N and bonus[0] == tgt[N - 1] and list(path[0, :N]) == list(range(N))
+    assert plen[1] == 1 and bonus[1] == 500 and path[1, 0] == 0 and (path[1, 1:] == -1).all()
+    assert plen[2] == 2 and path[2, 1] == 1 and bonus[2] == tgt[1]   # first of equal siblings
+    assert plen[3] == 0 and bonus[3] == -1 and (path[3] == -1).all()
+    assert st.cpu().tolist() == [0, 0, 0, tv.TV_STATUS_BAD_PARENT, 0]
+    # accepted path longer than P
+    st.zero_()
+    path, plen, bonus = tv.tv_tree_accept(i32_dev(chain[None]), i32_dev(all_match[None]),
+                                          i32_dev(tgt[None]), 16, dev_status=st[:1])
+    assert plen.item() == 0 and st[0].item() == tv.TV_STATUS_DEPTH
+    # single node
+    path, plen, bonus = _accept_gpu(np.array([[-1]], np.int32), np.array([[4]], np.int32),
+                                    np.array([[99]], np.int32), 4)
+    assert plen[0] == 1 and bonus[0] == 99 and list(path[0]) == [0, -1, -1, -1]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_8b_ragged8_N64", "qwen3_30b_a3b_B4_L4096_N1024"])
+def test_compact_bit_exact(name):
+    import tree_draft_verification_amd as tv
+    wl = WORKLOADS[name]
+    if name != "tiny_fp32":
+        wl = wl.replace(L_lo=min(wl.L_lo, 300), L_hi=min(wl.L_hi, 900))
+    a = attn_inputs(wl)
+    rng = np.random.default_rng(43)
+    tgt = rng.integers(0, 20, size=(wl.B, wl.N)).astype(np.int32)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt)
+    acc = oracle.tree_accept(a["parent"], draft, tgt, P=32)
+    k2, v2, lens2 = oracle.kv_compact(a["k_cache"], a["v_cache"], a["seq_lens"],
+                                      acc["path"], acc["path_len"])
+    k = to_dev(a["k_cache"], wl.dtype)
+    v = to_dev(a["v_cache"], wl.dtype)
+    lens = i32_dev(a["seq_lens"])
+    tv.tv_kv_compact(k, v, lens, i32_dev(acc["path"]), i32_dev(acc["path_len"]))
+    np.testing.assert_array_equal(lens.cpu().numpy(), lens2)
+    gk, gv = to_host_bits(k), to_host_bits(v)
+    if wl.dtype == "f32":   # NaN-poisoned rows: compare bits
+        gk, gv, k2, v2 = (x.view(np.uint32) for x in (gk, gv, k2, v2))
+    np.testing.assert_array_equal(gk, k2)
+    np.testing.assert_array_equal(gv, v2)
+
+
+def test_compact_hazard_every_row_moves():
+    """path = [0, 2, 4, 6, ...]: every move j reads the row a later move... and
+    an earlier move writes row path[j'] = j; staging must keep it exact."""
+    import tree_draft_verification_amd as tv
+    B, Hkv, D, L, N, P = 2, 3, 128, 5, 64, 32
+    rng = np.random.default_rng(44)
+    kc = rng.integers(0, 65535, size=(B, Hkv, L + N + 8, D)).astype(np.uint16)
+    vc = rng.integers(0, 65535, size=(B, Hkv, L + N + 8, D)).astype(np.uint16)
+    path = np.full((B, P), -1, np.int32)
+    path[0, :20] = np.arange(0, 40, 2)
+    path[1, :32] = np.concatenate([[0], np.arange(1, 32) + 30])
+    plen = np.array([20, 32], np.int32)
+    lens = np.array([L, L], np.int32)
+    k2, v2, lens2 = oracle.kv_compact(kc, vc, lens, path, plen)
+    k, v, sl = to_dev(kc, "bf16"), to_dev(vc, "bf16"), i32_dev(lens)
+    tv.tv_kv_compact(k, v, sl, i32_dev(path), i32_dev(plen))
+    np.testing.assert_array_equal(to_host_bits(k), k2)
+    np.testing.assert_array_equal(to_host_bits(v), v2)
+    np.testing.assert_array_equal(sl.cpu().numpy(), lens2)
+
+
+# ---------------------------------------------------------------- whole step
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "q8_ragged3_N64", "a3b_B2_L257_N200"])
+def test_step_end_to_end_small(name):
+    import tree_draft_verification_amd as tv
+    wl = ATTN_CASES[name]
+    if wl.dtype == "bf16":
+        wl = wl.replace(V=5000, hidden=512)
+    a = attn_inputs(wl)
+    lm = lmhead_inputs(wl)
+    ref_lm = oracle.lm_head_argmax(lm["hidden"], lm["w"], wl.dtype)
+    tgt_ref = ref_lm["argmax"].reshape(wl.B, wl.N)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt_ref)
+    ref = oracle.verify_step(a, lm, draft, wl.dtype)
+
+    q, k, v = (to_dev(a[x], wl.dtype) for x in ("q", "k_cache", "v_cache"))
+    lens = i32_dev(a["seq_lens"])
+    par = i32_dev(a["parent"])
+    out = tv.tv_tree_verify_attn(q, k, v, lens, par, max_seq_len=int(a["seq_lens"].max()),
+                                 scale=a["scale"])
+    arg = tv.tv_lmhead_argmax(to_dev(lm["hidden"], wl.dtype), to_dev(lm["w"], wl.dtype))
+    path, plen, bonus = tv.tv_tree_accept(par, i32_dev(draft), arg, 32)
+    tv.tv_kv_compact(k, v, lens, path, plen)
+
+    assert_attn_close(to_host_f64(out), ref["out"], name)
+    got_arg = arg.cpu().numpy()
+    assert_argmax_ok(got_arg, ref_lm, name)
+    # acceptance is checked against the oracle run on the GPU's argmax, which
+    # equals the oracle's own argmax except at exempt near-ties
+    acc = oracle.tree_accept(a["parent"], draft, got_arg.reshape(wl.B, wl.N), 32)
+    np.testing.assert_array_equal(plen.cpu().numpy(), acc["path_len"])
+    np.testing.assert_array_equal(path.cpu().numpy(), acc["path"])
+    np.testing.assert_array_equal(bonus.cpu().numpy(), acc["bonus"])
+    k2, v2, lens2 = oracle.kv_compact(a["k_cache"], a["v_cache"], a["seq_lens"],
+                                      acc["path"], acc["path_len"])
+    np.testing.assert_array_equal(lens.cpu().numpy(), lens2)
+    gk = to_host_bits(k)
+    if wl.dtype == "f32":
+        gk, k2 = gk.view(np.uint32), k2.view(np.uint32)
+    np.testing.assert_array_equal(gk, k2)

@@ -1,0 +1,214 @@
+"""Tree-verification step of tree speculative decoding on MI355X (gfx950).
+
+Thin Python binding over the C-ABI library libtreeverify.so (declared in
+include/treeverify.h).  Functions carry the C names; they check tensor
+shapes, pass raw device pointers and the current HIP stream, and raise
+TreeVerifyError on a negative status.  Every step of the computation runs in
+the library's HIP kernels; torch only provides device memory and streams.
+There is no CPU fallback: importing fails if the library is not built.
+
+One verification step (JetSpec GitHub README, "JetSpec > Overview"):
+    out        = tv_tree_verify_attn(q, k_cache, v_cache, seq_lens, parent, ...)
+    tgt        = tv_lmhead_argmax(hidden, w_vocab)
+    path, n, b = tv_tree_accept(parent, draft_tokens, tgt)
+    tv_kv_compact(k_cache, v_cache, seq_lens, path, n)
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import (TV_BF16, TV_F32, TV_MAX_NODES, TV_STATUS_BAD_LEN,  # noqa: F401
+                   TV_STATUS_BAD_PARENT, TV_STATUS_DEPTH)
+
+_LIB = _lib.load()
+
+__all__ = [
+    "TreeVerifyError", "tv_tree_verify_attn", "tv_tree_verify_attn_workspace",
+    "tv_lmhead_argmax", "tv_lmhead_argmax_workspace", "tv_tree_accept",
+    "tv_kv_compact", "tv_status_string", "tv_abi_version", "library_path",
+]
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {tv_status_string(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def tv_status_string(status: int) -> str:
+    return _LIB.tv_status_string(int(status)).decode()
+
+
+def tv_abi_version() -> int:
+    return int(_LIB.tv_abi_version())
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise TreeVerifyError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    if t.dtype == torch.float32:
+        return TV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _i32(t: torch.Tensor, shape, name: str):
+    if t.dtype != torch.int32 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be int32 of shape {tuple(shape)}, got "
+                         f"{t.dtype} {tuple(t.shape)}")
+
+
+_WS_CACHE: dict = {}
+
+
+def _cached_workspace(kind: str, nbytes: int, dev: torch.device) -> torch.Tensor:
+    """Zero-initialised device scratch reused across calls (grown on demand).
+
+    Calls that share it must be ordered on one stream; the LM-head call
+    returns its part to zero when it completes.
+    """
+    key = (kind, dev)
+    buf = _WS_CACHE.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _WS_CACHE[key] = buf
+    return buf
+
+
+# ---------------------------------------------------------------- attention
+
+def tv_tree_verify_attn_workspace(B, N, Hq, Hkv, D, max_seq_len, dtype=TV_BF16) -> int:
+    return int(_LIB.tv_tree_verify_attn_workspace(B, N, Hq, Hkv, D, max_seq_len, dtype))
+
+
+def tv_tree_verify_attn(q, k_cache, v_cache, seq_lens, parent, out=None, *,
+                        max_seq_len: int, scale: float | None = None,
+                        workspace: torch.Tensor | None = None,
+                        dev_status: torch.Tensor | None = None) -> torch.Tensor:
+    """Tree-causal attention.  q [B,N,Hq,D]; caches [B,Hkv,Lcap,D]."""
+    B, N, Hq, D = q.shape
+    Bk, Hkv, Lcap, Dk = k_cache.shape
+    if (Bk, Dk) != (B, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("q, k_cache and v_cache shapes disagree")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    _i32(seq_lens, (B,), "seq_lens")
+    _i32(parent, (B, N), "parent")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = tv_tree_verify_attn_workspace(B, N, Hq, Hkv, D, max_seq_len, dt)
+    if workspace is None and need > 0:
+        workspace = _cached_workspace("attn", need, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _LIB.tv_tree_verify_attn(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(parent), _ptr(out),
+        B, N, Hq, Hkv, D, Lcap, int(max_seq_len), float(scale), dt,
+        _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(q.device))
+    _check("tv_tree_verify_attn", st)
+    return out
+
+
+# ---------------------------------------------------------------- LM head
+
+def tv_lmhead_argmax_workspace(M, K, V, dtype=TV_BF16) -> int:
+    return int(_LIB.tv_lmhead_argmax_workspace(M, K, V, dtype))
+
+
+def tv_lmhead_argmax(hidden, w, argmax=None, logits=None, *,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """argmax[r] = argmax_v sum_k hidden[r,k] w[v,k].  hidden [M,K]; w [V,K].
+
+    A caller-supplied workspace must be zero-filled before its first use.
+    """
+    M, K = hidden.shape
+    V, Kw = w.shape
+    if Kw != K or w.dtype != hidden.dtype:
+        raise ValueError("hidden and w disagree in width or dtype")
+    dt = _dtype_code(hidden)
+    if argmax is None:
+        argmax = torch.empty(M, dtype=torch.int32, device=hidden.device)
+    _i32(argmax, (M,), "argmax")
+    if logits is not None and (logits.dtype != torch.float32 or tuple(logits.shape) != (M, V)):
+        raise ValueError("logits must be float32 of shape (M, V)")
+    need = tv_lmhead_argmax_workspace(M, K, V, dt)
+    if workspace is None:
+        workspace = _cached_workspace("lmhead", need, hidden.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _LIB.tv_lmhead_argmax(_ptr(hidden), _ptr(w), _ptr(argmax), _ptr(logits), M, K, V, dt,
+                               _ptr(workspace), ws_bytes, _stream(hidden.device))
+    _check("tv_lmhead_argmax", st)
+    return argmax
+
+
+# ---------------------------------------------------------------- accept
+
+def tv_tree_accept(parent, draft_tokens, target_tokens, P: int = 32, *, path=None,
+                   path_len=None, bonus=None, dev_status=None):
+    """Longest accepted path + bonus token; returns (path [B,P], path_len [B], bonus [B])."""
+    B, N = parent.shape
+    _i32(parent, (B, N), "parent")
+    _i32(draft_tokens, (B, N), "draft_tokens")
+    target_tokens = target_tokens.reshape(B, N)
+    _i32(target_tokens, (B, N), "target_tokens")
+    dev = parent.device
+    if path is None:
+        path = torch.empty((B, P), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    _i32(path, (B, P), "path")
+    _i32(path_len, (B,), "path_len")
+    _i32(bonus, (B,), "bonus")
+    st = _LIB.tv_tree_accept(_ptr(parent), _ptr(draft_tokens), _ptr(target_tokens),
+                             _ptr(path), _ptr(path_len), _ptr(bonus), B, N, P,
+                             _ptr(dev_status), _stream(dev))
+    _check("tv_tree_accept", st)
+    return path, path_len, bonus
+
+
+# ---------------------------------------------------------------- compaction
+
+def tv_kv_compact(k_cache, v_cache, seq_lens, path, path_len) -> None:
+    """Move the accepted rows to L_b + j in place and add path_len to seq_lens."""
+    B, Hkv, Lcap, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache disagree")
+    dt = _dtype_code(k_cache)
+    _i32(seq_lens, (B,), "seq_lens")
+    P = path.shape[1]
+    _i32(path, (B, P), "path")
+    _i32(path_len, (B,), "path_len")
+    st = _LIB.tv_kv_compact(_ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(path),
+                            _ptr(path_len), B, Hkv, D, Lcap, P, dt, _stream(k_cache.device))
+    _check("tv_kv_compact", st)

@@ -1,0 +1,42 @@
+"""ctypes handle on libtreeverify.so with the C signatures of include/treeverify.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libtreeverify.so")
+
+TV_OK, TV_EINVAL, TV_ENOTSUP, TV_EWORKSPACE, TV_EHIP = 0, -1, -2, -3, -4
+TV_BF16, TV_F32 = 0, 1
+TV_STATUS_BAD_PARENT, TV_STATUS_BAD_LEN, TV_STATUS_DEPTH = 1, 2, 4
+TV_MAX_NODES = 1024
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_f = ctypes.c_float
+
+SIGNATURES = {
+    "tv_tree_verify_attn_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "tv_tree_verify_attn": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                                 _p, _sz, _p, _p]),
+    "tv_lmhead_argmax_workspace": (_sz, [_i, _i, _i, _i]),
+    "tv_lmhead_argmax": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p, _sz, _p]),
+    "tv_tree_accept": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p]),
+    "tv_kv_compact": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
+    "tv_status_string": (ctypes.c_char_p, [_i]),
+    "tv_abi_version": (_i, []),
+}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m tree_draft_verification_amd.build); there is no fallback")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib

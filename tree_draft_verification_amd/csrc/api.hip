@@ -1,0 +1,115 @@
+// Public C ABI (include/treeverify.h): host-side validation, then launches.
+// Every check here runs before any HIP call, so a rejected call has no
+// effect on the device or the stream.
+#include <math.h>
+#include <stdio.h>
+
+#include "tv_internal.h"
+
+namespace {
+
+thread_local char g_hip_msg[256];
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return TV_OK;
+  snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP launch failed: %s (%d)", hipGetErrorString(e),
+           (int)e);
+  return TV_EHIP;
+}
+
+bool dtype_ok(int dtype) { return dtype == TV_BF16 || dtype == TV_F32; }
+
+}  // namespace
+
+extern "C" {
+
+int tv_abi_version(void) { return 10000; }
+
+const char* tv_status_string(int status) {
+  switch (status) {
+    case TV_OK: return "ok";
+    case TV_EINVAL: return "invalid argument (shape, size or null pointer)";
+    case TV_ENOTSUP: return "unsupported configuration (head dim, dtype, node count or k)";
+    case TV_EWORKSPACE: return "workspace missing or too small";
+    case TV_EHIP: return g_hip_msg[0] ? g_hip_msg : "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t tv_tree_verify_attn_workspace(int B, int N, int Hq, int Hkv, int D, int max_seq_len,
+                                     int dtype) {
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_seq_len < 0) return 0;
+  return tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype).ws_bytes;
+}
+
+int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, const int32_t* parent, void* out, int B,
+                        int N, int Hq, int Hkv, int D, int Lcap, int max_seq_len, float scale,
+                        int dtype, void* workspace, size_t ws_bytes, int32_t* dev_status,
+                        void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !parent || !out) return TV_EINVAL;
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || D < 1 || Lcap < 1 || max_seq_len < 0)
+    return TV_EINVAL;
+  if (Hq % Hkv) return TV_EINVAL;
+  if ((long long)max_seq_len + N > Lcap) return TV_EINVAL;
+  if (!isfinite(scale)) return TV_EINVAL;
+  if (!dtype_ok(dtype)) return TV_ENOTSUP;
+  if (D != 64 && D != 128) return TV_ENOTSUP;
+  if (N > TV_MAX_NODES) return TV_ENOTSUP;
+  if (dtype == TV_F32 && ((long long)N * Hq > 2147483647LL || B > 65535 || Hq > 65535))
+    return TV_ENOTSUP;
+  const tv::AttnPlan plan = tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype);
+  if ((long long)B * Hkv * plan.nqblk * plan.nsplit > 2147483647LL) return TV_ENOTSUP;
+  if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes)) return TV_EWORKSPACE;
+  return hip_status(tv::launch_tree_attn(q, k_cache, v_cache, seq_lens, parent, out, B, N, Hq,
+                                         Hkv, D, Lcap, max_seq_len, scale, dtype, plan,
+                                         workspace, dev_status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype) {
+  if (M < 1) return 0;
+  return tv::lmhead_ws_bytes(M, K, V, dtype);
+}
+
+int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax, float* logits, int M,
+                     int K, int V, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+  if (!hidden || !w || !argmax) return TV_EINVAL;
+  if (M < 1 || K < 1 || V < 1) return TV_EINVAL;
+  if (!dtype_ok(dtype)) return TV_ENOTSUP;
+  if (dtype == TV_BF16 && K % 128) return TV_ENOTSUP;
+  const long long blocks = dtype == TV_BF16
+                               ? (long long)((M + 63) / 64) * ((V + 127) / 128)
+                               : (long long)((M + 15) / 16) * ((V + 255) / 256);
+  if (blocks > 2147483647LL) return TV_ENOTSUP;
+  if (!workspace || ws_bytes < tv::lmhead_ws_bytes(M, K, V, dtype)) return TV_EWORKSPACE;
+  return hip_status(tv::launch_lmhead_argmax(hidden, w, argmax, logits, M, K, V, dtype,
+                                             workspace, static_cast<hipStream_t>(stream)));
+}
+
+int tv_tree_accept(const int32_t* parent, const int32_t* draft_tokens,
+                   const int32_t* target_tokens, int32_t* path, int32_t* path_len,
+                   int32_t* bonus, int B, int N, int P, int32_t* dev_status, void* stream) {
+  if (!parent || !draft_tokens || !target_tokens || !path || !path_len || !bonus)
+    return TV_EINVAL;
+  if (B < 1 || N < 1 || P < 1) return TV_EINVAL;
+  if (N > TV_MAX_NODES || P > 64 || B > 2147483647) return TV_ENOTSUP;
+  return hip_status(tv::launch_tree_accept(parent, draft_tokens, target_tokens, path, path_len,
+                                           bonus, B, N, P, dev_status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int tv_kv_compact(void* k_cache, void* v_cache, int32_t* seq_lens, const int32_t* path,
+                  const int32_t* path_len, int B, int Hkv, int D, int Lcap, int P, int dtype,
+                  void* stream) {
+  if (!k_cache || !v_cache || !seq_lens || !path || !path_len) return TV_EINVAL;
+  if (B < 1 || Hkv < 1 || D < 1 || Lcap < 1 || P < 1) return TV_EINVAL;
+  if (!dtype_ok(dtype)) return TV_ENOTSUP;
+  const int esz = dtype == TV_F32 ? 4 : 2;
+  if ((D * esz) % 16 || P > 64 || (long long)P * D * esz > 65536) return TV_ENOTSUP;
+  if (B > 65535 || Hkv > 2147483647) return TV_ENOTSUP;
+  return hip_status(tv::launch_kv_compact(k_cache, v_cache, seq_lens, path, path_len, B, Hkv, D,
+                                          Lcap, P, dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

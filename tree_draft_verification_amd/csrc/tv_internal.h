@@ -1,0 +1,106 @@
+// Internal declarations of the gfx950 tree-verification library.
+// Nothing here is part of the public C ABI (include/treeverify.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "treeverify.h"
+
+namespace tv {
+
+// ---------------------------------------------------------------- bf16 bits
+
+typedef uint16_t bf16_t;  // bf16 storage: raw bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------- MFMA types
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+union Frag8 {  // eight bf16 values as one MFMA operand or one 16-byte load
+  uint4 u;
+  bf16x8_t v;
+};
+
+// D = A(16x32) * B(32x16) + C on the matrix cores.  Lane l holds row/column
+// l % 16 and the eight k values 8*(l/16)..8*(l/16)+7 of each operand; the
+// result lane l holds column l % 16, rows 4*(l/16)..4*(l/16)+3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- launch helpers
+
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+
+// The dispatcher hands workgroup `bid` to die bid % 8.  Returns a logical index
+// such that consecutive logical indices run on the same die (so workgroups that
+// share data share that die's L2).  A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  const int xcd = bid % kXcds;
+  const int slot = bid / kXcds;
+  const int per = total / kXcds;
+  const int rem = total % kXcds;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Packed (value, index) key: the maximum key is the largest value, and among
+// equal values the smallest index.
+__device__ __forceinline__ unsigned long long argmax_key(float f, uint32_t idx) {
+  return ((unsigned long long)f32_order_key(f) << 32) | (unsigned long long)(~idx);
+}
+
+// ---------------------------------------------------------------- launchers
+
+struct AttnPlan {
+  int nqblk;      // query blocks of 128 rows per (sequence, KV head)
+  int nsplit;     // workgroups along the prefix per query block
+  int chunk_len;  // prefix keys per split (multiple of 64)
+  size_t ws_bytes;
+};
+
+AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dtype);
+
+hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
+                            const int32_t* seq_lens, const int32_t* parent,
+                            void* out, int B, int N, int Hq, int Hkv, int D,
+                            int Lcap, int max_seq_len, float scale, int dtype,
+                            const AttnPlan& plan, void* ws, int32_t* dev_status,
+                            hipStream_t stream);
+
+size_t lmhead_ws_bytes(int M, int K, int V, int dtype);
+
+hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
+                                float* logits, int M, int K, int V, int dtype,
+                                void* ws, hipStream_t stream);
+
+hipError_t launch_tree_accept(const int32_t* parent, const int32_t* draft,
+                              const int32_t* tgt, int32_t* path, int32_t* path_len,
+                              int32_t* bonus, int B, int N, int P,
+                              int32_t* dev_status, hipStream_t stream);
+
+hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t* path,
+                             const int32_t* path_len, int B, int Hkv, int D,
+                             int Lcap, int P, int dtype, hipStream_t stream);
+
+}  // namespace tv
