@@ -1,0 +1,281 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-verification step on one MI355X.
+
+One step = tv_tree_verify_attn -> tv_lmhead_argmax -> tv_tree_accept ->
+tv_kv_compact on one stream, over one batch of synthetic inputs already
+resident in HBM (the Qwen3-8B-shaped layer with a 1024-token prefix and a
+64-node draft tree by default).  Prints one JSON line with verified tree
+nodes/s, the step time, the roofline fraction of the dominant kernel (the
+LM head, whose per-launch time is taken with HIP events on the launch
+stream), and the fp64 oracle timed on this host's cores as a CPU baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
+FP32_VEC_TFLOPS = 157.3
+METRIC = "verified tree nodes/s + verify-step µs on 1 MI355X; % of HBM/MFMA roofline"
+DEFAULT_WORKLOAD = "qwen3_8b_L1024_N64"
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+LMHEAD_SOURCES = [os.path.join(ROOT, "tree_draft_verification_amd", "csrc", f)
+                  for f in ("lmhead.hip", "tv_internal.h")]
+
+
+def kernel_source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_work(wl, a, path, path_len):
+    """Bytes and flops each part must move / compute (not what it wastes)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    L = a["seq_lens"].astype(np.int64)
+    depth = a["depth"].astype(np.int64)
+    attn_bytes = int((2 * L * wl.Hkv * wl.D * e).sum()
+                     + wl.B * wl.N * (2 * wl.Hq * wl.D * e + 2 * wl.Hkv * wl.D * e + 4))
+    attn_flops = int(4 * wl.Hq * wl.D * (L[:, None] + depth + 1).sum())
+    lm_bytes = int(wl.V * wl.hidden * e + wl.M * wl.hidden * e + 4 * wl.M)
+    lm_flops = int(2 * wl.M * wl.hidden * wl.V)
+    moved = sum(int((path[b, :path_len[b]] != np.arange(path_len[b])).sum())
+                for b in range(wl.B))
+    compact_bytes = int(4 * moved * wl.Hkv * wl.D * e + 8 * wl.B)
+    accept_bytes = int(12 * wl.B * wl.N + 4 * wl.B * (path.shape[1] + 2))
+    return dict(attn=(attn_bytes, attn_flops), lmhead=(lm_bytes, lm_flops),
+                accept=(accept_bytes, 0), compact=(compact_bytes, 0))
+
+
+def roof_entry(nbytes, flops, us, dtype):
+    t = us * 1e-6
+    gbs = nbytes / t / 1e9
+    tflops = flops / t / 1e12
+    peak_f = BF16_DENSE_TFLOPS if dtype == "bf16" else FP32_VEC_TFLOPS
+    t_roof = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (peak_f * 1e12))
+    bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (peak_f * 1e12) else "mfma"
+    return dict(us=round(us, 2), bytes=nbytes, flops=flops, gbs=round(gbs, 1),
+                tflops=round(tflops, 2), bound=bound, roof_us=round(t_roof * 1e6, 2),
+                frac=round(t_roof / t, 4))
+
+
+def cpu_baseline(wl, a, lm, coins, budget_s=20.0):
+    """The fp64 oracle, as it stands, on whole verification steps of the
+    same workload, repeated until about budget_s seconds have passed."""
+    import oracle
+    from workloads import draft_tokens
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    reps, spent = 0, 0.0
+    while reps < 20 and (reps == 0 or spent < budget_s):
+        t0 = time.perf_counter()
+        oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"], a["parent"],
+                              a["scale"], wl.dtype)
+        ref = oracle.lm_head_argmax(lm["hidden"], lm["w"], wl.dtype)
+        t1 = time.perf_counter()
+        tgt = ref["argmax"].reshape(wl.B, wl.N)
+        draft = draft_tokens(a["parent"], coins, tgt)           # drafter input, untimed
+        t2 = time.perf_counter()
+        acc = oracle.tree_accept(a["parent"], draft, tgt, 32)
+        oracle.kv_compact(a["k_cache"], a["v_cache"], a["seq_lens"], acc["path"],
+                          acc["path_len"])
+        t3 = time.perf_counter()
+        spent += (t1 - t0) + (t3 - t2)
+        reps += 1
+    return dict(value=round(wl.M * reps / spent, 3), unit="nodes/s", cores=int(cores),
+                kind="oracle",
+                sample=f"{reps} whole verification step(s) of {wl.name} "
+                       f"({wl.M} nodes each, {spent:.1f} s of fp64 numpy)")
+
+
+def copy_calibration(nbytes: int, reps: int = 5) -> None:
+    """A plain device copy of known size, to scale HBM counters against."""
+    import torch
+    n = nbytes // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0,
+                    help="only run a plain device copy of this many bytes")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the step has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        copy_calibration(args.calibrate_copy)
+        return
+
+    import torch
+
+    import tree_draft_verification_amd as tv
+    from workloads import WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    a = attn_inputs(wl)
+    lm = lmhead_inputs(wl)
+    coins = draft_coins(wl, a["depth"])
+
+    def to_dev(x):
+        x = np.ascontiguousarray(x)
+        if wl.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+    q, kc, vc = to_dev(a["q"]), to_dev(a["k_cache"]), to_dev(a["v_cache"])
+    hid, w = to_dev(lm["hidden"]), to_dev(lm["w"])
+    # The vocabulary projection is a static weight: repack it once, outside
+    # the timed region, into the layout the LM-head kernel streams fastest.
+    w_step = tv.tv_lmhead_pack_weights(w) if wl.dtype == "bf16" else w
+    lens0 = i32(a["seq_lens"])
+    lens = lens0.clone()
+    parent = i32(a["parent"])
+    max_len = int(a["seq_lens"].max())
+    out = torch.empty_like(q)
+    argmax = torch.empty(wl.M, dtype=torch.int32, device=dev)
+    P = 32
+    path = torch.empty((wl.B, P), dtype=torch.int32, device=dev)
+    plen = torch.empty(wl.B, dtype=torch.int32, device=dev)
+    bonus = torch.empty(wl.B, dtype=torch.int32, device=dev)
+    dt = tv.TV_BF16 if wl.dtype == "bf16" else tv.TV_F32
+    attn_ws = torch.zeros(max(256, tv.tv_tree_verify_attn_workspace(
+        wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, max_len, dt)), dtype=torch.uint8, device=dev)
+    lm_ws = torch.zeros(tv.tv_lmhead_argmax_workspace(wl.M, wl.hidden, wl.V, dt),
+                        dtype=torch.uint8, device=dev)
+
+    # Draft tokens of the simulated drafter: they copy the target's greedy
+    # token at the parent (from one untimed LM-head call) with the workload's
+    # probability, else a random token.
+    tv.tv_lmhead_argmax(hid, w_step, argmax, workspace=lm_ws)
+    draft = i32(draft_tokens(a["parent"], coins, argmax.cpu().numpy().reshape(wl.B, wl.N)))
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+          for _ in range(args.steps)]
+
+    def step(events=None):
+        lens.copy_(lens0)   # compaction advanced the lengths; restore the batch
+        if events:
+            events[0].record()
+        tv.tv_tree_verify_attn(q, kc, vc, lens, parent, out, max_seq_len=max_len,
+                               scale=a["scale"], workspace=attn_ws)
+        if events:
+            events[1].record()
+        tv.tv_lmhead_argmax(hid, w_step, argmax, workspace=lm_ws)
+        if events:
+            events[2].record()
+        tv.tv_tree_accept(parent, draft, argmax, P, path=path, path_len=plen, bonus=bonus)
+        if events:
+            events[3].record()
+        tv.tv_kv_compact(kc, vc, lens, path, plen)
+        if events:
+            events[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    # For reference only: the same LM head reading the row-major weight.
+    rm_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rm_reps = 20
+    rm_ev[0].record()
+    for _ in range(rm_reps):
+        tv.tv_lmhead_argmax(hid, w, argmax, workspace=lm_ws)
+    rm_ev[1].record()
+    torch.cuda.synchronize()
+    lm_rowmajor_us = rm_ev[0].elapsed_time(rm_ev[1]) * 1e3 / rm_reps
+
+    names = ["attn", "lmhead", "accept", "compact"]
+    per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+           * 1e3 for j, n in enumerate(names)}
+    step_us = float(np.mean([ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)])) * 1e3
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    value = wl.M * args.steps / (t1 - t0)
+
+    path_h, plen_h = path.cpu().numpy(), plen.cpu().numpy()
+    work = algorithmic_work(wl, a, path_h, plen_h)
+    kernels = {n: roof_entry(work[n][0], work[n][1], per[n], wl.dtype) for n in names}
+
+    # Dominant kernel: the LM head (one kernel launch per call).
+    lm_b, lm_f = work["lmhead"]
+    lm_us = per["lmhead"]
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            cnt = json.load(f).get("lmhead_bf16_kernel", {})
+        if (cnt.get("workload") == wl.name
+                and cnt.get("source_digest") == kernel_source_digest(LMHEAD_SOURCES)):
+            traffic = cnt.get("traffic_bytes")
+    mfma_bound = lm_f / (BF16_DENSE_TFLOPS * 1e12) > lm_b / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        achieved = lm_f / (lm_us * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_DENSE_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / BF16_DENSE_TFLOPS, 4),
+                    traffic=traffic)
+    else:
+        achieved = lm_b / (lm_us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
+    roof.update(kernel="lmhead_bf16_kernel<packed>" if wl.dtype == "bf16" else "lmhead_f32_kernel",
+                algorithmic_bytes=lm_b, launch_us=round(lm_us, 2))
+
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "config": {"workload": wl.name, "batch": wl.B, "nodes": wl.N,
+                   "prefix": [int(x) for x in a["seq_lens"]], "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "head_dim": wl.D, "hidden": wl.hidden, "vocab": wl.V,
+                   "parallelism": "none (1 GPU)"},
+        "step_us": round(step_us, 2),
+        "mean_path_len": float(plen_h.mean()),
+        "roofline": roof,
+        "kernels": kernels,
+        "lmhead_rowmajor_us": round(lm_rowmajor_us, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, a, lm, coins)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -50,6 +50,9 @@ extern "C" {
 #define TV_BF16 0
 #define TV_F32  1
 
+#define TV_LAYOUT_ROWMAJOR 0 /* w is [V][K], one row per vocabulary entry     */
+#define TV_LAYOUT_PACKED   1 /* w as written by tv_lmhead_pack_weights        */
+
 #define TV_STATUS_BAD_PARENT 1 /* parent[0] != -1 or parent[i] not in [0, i) */
 #define TV_STATUS_BAD_LEN    2 /* L_b < 0, L_b > max_seq_len or L_b+N > Lcap */
 #define TV_STATUS_DEPTH      4 /* accepted path longer than P                */
@@ -99,20 +102,38 @@ int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
  *   argmax[r]    = smallest v attaining max_v logits[r][v]
  *
  * hidden  [M][K] dtype, row r = b*N + i for node i of sequence b
- * w       [V][K] dtype (one row per vocabulary entry)
+ * w       the vocabulary projection in layout `w_layout`:
+ *         TV_LAYOUT_ROWMAJOR: [V][K] dtype, one row per vocabulary entry;
+ *         TV_LAYOUT_PACKED:   the buffer written by tv_lmhead_pack_weights
+ *                             (bf16 only), the faster form for a weight that
+ *                             is reused across steps
  * argmax  [M] int32 (written)
  * logits  [M][V] fp32 or NULL; written only when non-NULL (for checking:
  *         the step itself never materialises the logits)
  * workspace  at least tv_lmhead_argmax_workspace() bytes.  It must be
  *         zero-filled before its first use; every call leaves it zero-filled
  *         again when its kernel completes, so one buffer serves any number of
- *         calls in stream order.
- * Supported: bf16 needs K % 128 == 0; M >= 1, V >= 1.
+ *         calls in stream order (calls sharing it must not overlap).
+ * Supported: bf16 needs K % 256 == 0; M >= 1, V >= 1.
  */
 size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype);
 int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
                      float* logits, int M, int K, int V, int dtype,
-                     void* workspace, size_t ws_bytes, void* stream);
+                     int w_layout, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * Repack a row-major bf16 vocabulary projection [V][K] into the layout the
+ * LM-head kernel streams fastest: for every tile of 128 rows and every
+ * 128-wide k chunk, the 32 KB the kernel reads are stored contiguously in
+ * the order its lanes consume them (rows past V are zero).  Done once per
+ * weight; `w_packed` (device, tv_lmhead_packed_bytes() bytes, caller-owned)
+ * must not overlap `w`.  Returns TV_ENOTSUP unless dtype is TV_BF16 and
+ * K % 256 == 0 (tv_lmhead_packed_bytes then returns 0).
+ */
+size_t tv_lmhead_packed_bytes(int V, int K, int dtype);
+int tv_lmhead_pack_weights(const void* w, void* w_packed, int V, int K,
+                           int dtype, void* stream);
 
 /*
  * Greedy longest-accepted-path selection plus the bonus token (JetSpec GitHub

@@ -39,6 +39,7 @@ def test_header_declares_the_four_calls():
     names = _declared_functions()
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
+              "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
               "tv_status_string", "tv_abi_version"):
         assert n in names
 
@@ -95,13 +96,29 @@ def test_lmhead_host_validation(lib):
     ws = lib.tv_lmhead_argmax_workspace(64, 4096, 151936, 0)
     assert ws >= 64 * 8
     f = lib.tv_lmhead_argmax
-    assert f(None, FAKE, FAKE, None, 64, 4096, 151936, 0, FAKE, ws, None) == -1
-    assert f(FAKE, FAKE, None, None, 64, 4096, 151936, 0, FAKE, ws, None) == -1
-    assert f(FAKE, FAKE, FAKE, None, 0, 4096, 151936, 0, FAKE, ws, None) == -1
-    assert f(FAKE, FAKE, FAKE, None, 64, 4000, 151936, 0, FAKE, ws, None) == -2
-    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 5, FAKE, ws, None) == -2
-    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, None, ws, None) == -3
-    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, FAKE, ws - 1, None) == -3
+    assert f(None, FAKE, FAKE, None, 64, 4096, 151936, 0, 0, FAKE, ws, None) == -1
+    assert f(FAKE, FAKE, None, None, 64, 4096, 151936, 0, 0, FAKE, ws, None) == -1
+    assert f(FAKE, FAKE, FAKE, None, 0, 4096, 151936, 0, 0, FAKE, ws, None) == -1
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, 2, FAKE, ws, None) == -1   # layout
+    assert f(FAKE, FAKE, FAKE, None, 64, 4000, 151936, 0, 0, FAKE, ws, None) == -2
+    assert f(FAKE, FAKE, FAKE, None, 64, 4224, 151936, 0, 1, FAKE, ws, None) == -2   # K % 256
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 5, 0, FAKE, ws, None) == -2
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 1, 1, FAKE, ws, None) == -2   # f32 packed
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, 0, None, ws, None) == -3
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, 0, FAKE, ws - 1, None) == -3
+
+
+def test_pack_host_validation(lib):
+    assert lib.tv_lmhead_packed_bytes(151936, 4096, 0) == 151936 * 4096 * 2
+    assert lib.tv_lmhead_packed_bytes(1000, 256, 0) == 1024 * 256 * 2      # whole 128-row tiles
+    assert lib.tv_lmhead_packed_bytes(1000, 384, 0) == 0
+    assert lib.tv_lmhead_packed_bytes(1000, 256, 1) == 0
+    p = lib.tv_lmhead_pack_weights
+    assert p(None, FAKE, 1000, 256, 0, None) == -1
+    assert p(FAKE, FAKE, 1000, 256, 0, None) == -1                         # in place
+    assert p(FAKE, ctypes.c_void_p(0x2000), 0, 256, 0, None) == -1
+    assert p(FAKE, ctypes.c_void_p(0x2000), 1000, 384, 0, None) == -2
+    assert p(FAKE, ctypes.c_void_p(0x2000), 1000, 256, 1, None) == -2
 
 
 def test_accept_and_compact_host_validation(lib):
@@ -121,6 +138,7 @@ def test_binding_names_match_the_c_calls():
     import tree_draft_verification_amd as tv
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
+              "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
               "tv_status_string", "tv_abi_version"):
         assert callable(getattr(tv, n))
     assert tv.tv_status_string(-3) == "workspace missing or too small"

@@ -1,0 +1,117 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times.  Where the fp64 oracle cannot do every output in
+seconds, it computes sampled nodes / rows one by one; acceptance and
+compaction are always checked in full (bit-exact).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs
+
+from _helpers import (LOGITS_REL_L2, assert_argmax_ok, assert_attn_close, i32_dev, to_dev,
+                      to_host_bits, to_host_f64)
+
+pytestmark = pytest.mark.gpu
+
+NAMES = list(WORKLOADS)
+# nodes per sequence whose attention output the oracle recomputes
+ATTN_SAMPLE = {"tiny_fp32": None, "qwen3_8b_L1024_N64": None, "qwen3_8b_L16384_N256": 48,
+               "qwen3_8b_ragged8_N64": 12, "qwen3_30b_a3b_B4_L4096_N1024": 16}
+# hidden-state rows whose logits the oracle recomputes
+LM_SAMPLE = {"tiny_fp32": None, "qwen3_8b_L1024_N64": 8, "qwen3_8b_L16384_N256": 16,
+             "qwen3_8b_ragged8_N64": 16, "qwen3_30b_a3b_B4_L4096_N1024": 16}
+
+_CACHE = {}
+
+
+def _inputs(name):
+    if name not in _CACHE:
+        wl = WORKLOADS[name]
+        a = attn_inputs(wl)
+        lm = lmhead_inputs(wl)
+        ref_lm = oracle.lm_head_argmax(lm["hidden"], lm["w"], wl.dtype)
+        _CACHE.clear()
+        _CACHE[name] = (wl, a, lm, ref_lm)
+    return _CACHE[name]
+
+
+def _sample(n, k, seed):
+    if k is None or k >= n:
+        return np.arange(n)
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=k - 2, replace=False)]))
+
+
+def _oracle_logits_rows(lm, rows, dtype, chunk=8192):
+    V = lm["w"].shape[0]
+    out = np.empty((len(rows), V))
+    for v0 in range(0, V, chunk):
+        out[:, v0:v0 + chunk] = oracle.lm_logits(lm["hidden"], lm["w"][v0:v0 + chunk], dtype,
+                                                 rows=rows)
+    return out
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_full_size_step(name):
+    """The step as the benchmark runs it (packed vocabulary projection for
+    bf16); the row-major layout is checked on the argmax as well."""
+    import torch
+    import tree_draft_verification_amd as tv
+    wl, a, lm, ref_lm = _inputs(name)
+    print(f"[full] {name}: B={wl.B} N={wl.N} L={list(a['seq_lens'])} M={wl.M} "
+          f"K={wl.hidden} V={wl.V}", flush=True)
+    tgt_ref = ref_lm["argmax"].reshape(wl.B, wl.N)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt_ref)
+
+    q, k, v = (to_dev(a[x], wl.dtype) for x in ("q", "k_cache", "v_cache"))
+    h, w = to_dev(lm["hidden"], wl.dtype), to_dev(lm["w"], wl.dtype)
+    lens, par = i32_dev(a["seq_lens"]), i32_dev(a["parent"])
+    st = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+    out = tv.tv_tree_verify_attn(q, k, v, lens, par, max_seq_len=int(a["seq_lens"].max()),
+                                 scale=a["scale"], dev_status=st)
+    logits = torch.empty((wl.M, wl.V), dtype=torch.float32, device="cuda")
+    w_step = tv.tv_lmhead_pack_weights(w) if wl.dtype == "bf16" else w
+    arg = tv.tv_lmhead_argmax(h, w_step, logits=logits)
+    arg_rm = tv.tv_lmhead_argmax(h, w)
+    path, plen, bonus = tv.tv_tree_accept(par, i32_dev(draft), arg, 32, dev_status=st)
+    tv.tv_kv_compact(k, v, lens, path, plen)
+    torch.cuda.synchronize()
+    assert st.cpu().numpy().tolist() == [0] * wl.B
+
+    # attention: sampled nodes (all of them where cheap)
+    nodes = _sample(wl.N, ATTN_SAMPLE[name], wl.seed)
+    ref_o = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"],
+                                  a["parent"], a["scale"], wl.dtype, nodes=nodes)
+    mx, rel = assert_attn_close(to_host_f64(out), ref_o, name)
+    print(f"[full] {name}: attention max|d|={mx:.2e} rel={rel:.2e} on {len(nodes)} nodes/seq",
+          flush=True)
+
+    # LM head: argmax of every row, logits of sampled rows
+    got_arg = arg.cpu().numpy()
+    ndiff = assert_argmax_ok(got_arg, ref_lm, name)
+    np.testing.assert_array_equal(arg_rm.cpu().numpy(), got_arg)
+    rows = _sample(wl.M, LM_SAMPLE[name], wl.seed + 1)
+    ref_l = _oracle_logits_rows(lm, rows, wl.dtype)
+    got_l = logits[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    lrel = np.linalg.norm(got_l - ref_l) / np.linalg.norm(ref_l)
+    assert lrel <= LOGITS_REL_L2, f"logits rel L2 {lrel:.3e}"
+    print(f"[full] {name}: logits rel={lrel:.2e}, argmax exempt-diffs={ndiff}", flush=True)
+
+    # acceptance + compaction, bit-exact, from the oracle fed the GPU argmax
+    acc = oracle.tree_accept(a["parent"], draft, got_arg.reshape(wl.B, wl.N), 32)
+    np.testing.assert_array_equal(plen.cpu().numpy(), acc["path_len"])
+    np.testing.assert_array_equal(path.cpu().numpy(), acc["path"])
+    np.testing.assert_array_equal(bonus.cpu().numpy(), acc["bonus"])
+    if ndiff == 0:
+        acc0 = oracle.tree_accept(a["parent"], draft, tgt_ref, 32)
+        np.testing.assert_array_equal(acc0["path"], acc["path"])
+    k2, v2, lens2 = oracle.kv_compact(a["k_cache"], a["v_cache"], a["seq_lens"], acc["path"],
+                                      acc["path_len"])
+    np.testing.assert_array_equal(lens.cpu().numpy(), lens2)
+    gk, gv = to_host_bits(k), to_host_bits(v)
+    if wl.dtype == "f32":
+        gk, gv, k2, v2 = (x.view(np.uint32) for x in (gk, gv, k2, v2))
+    np.testing.assert_array_equal(gk, k2)
+    np.testing.assert_array_equal(gv, v2)
+    print(f"[full] {name}: path_len={acc['path_len'].tolist()}", flush=True)

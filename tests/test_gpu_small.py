@@ -122,23 +122,28 @@ LM_CASES = {
     "tiny_fp32": WORKLOADS["tiny_fp32"],
     "M64_K4096_V8192": Q8.replace(V=8192, seed=31),
     "M100_K256_V1001": Q8.replace(B=1, N=100, hidden=256, V=1001, seed=32),
-    "M1_K128_V130": Q8.replace(N=1, hidden=128, V=130, seed=33),
+    "M1_K256_V130": Q8.replace(N=1, hidden=256, V=130, seed=33),
     "M256_K512_V4163": Q8.replace(N=256, hidden=512, V=4163, seed=34),
-    "M513_K128_V2000": Q8.replace(B=1, N=513, hidden=128, V=2000, seed=35),
+    "M513_K256_V2000": Q8.replace(B=1, N=513, hidden=256, V=2000, seed=35),
     "f32_M40_K100_V777": Q8.replace(dtype="f32", N=40, hidden=100, V=777, seed=36),
 }
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("name", list(LM_CASES))
-def test_lmhead_elementwise(name):
+def test_lmhead_elementwise(name, packed):
     import torch
     import tree_draft_verification_amd as tv
     wl = LM_CASES[name]
+    if packed and wl.dtype != "bf16":
+        pytest.skip("the packed layout is bf16 only")
     lm = lmhead_inputs(wl)
     M, V = wl.M, wl.V
     print(f"[lmhead] {name} M={M} K={wl.hidden} V={V}", flush=True)
     h = to_dev(lm["hidden"], wl.dtype)
     w = to_dev(lm["w"], wl.dtype)
+    if packed:
+        w = tv.tv_lmhead_pack_weights(w)
     logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
     ws = torch.zeros(tv.tv_lmhead_argmax_workspace(M, wl.hidden, V), dtype=torch.uint8,
                      device="cuda")
@@ -155,11 +160,27 @@ def test_lmhead_elementwise(name):
     np.testing.assert_array_equal(arg2.cpu().numpy(), arg.cpu().numpy())
 
 
+def test_pack_layout_matches_definition():
+    """Packed bytes = W (zero-padded to 128-row tiles) permuted to
+    [tile][k chunk][16-row block][16-byte piece][lane][8 values]."""
+    import tree_draft_verification_amd as tv
+    rng = np.random.default_rng(38)
+    V, K = 300, 512
+    w = rng.integers(0, 65535, size=(V, K)).astype(np.uint16)
+    got = tv.tv_lmhead_pack_weights(to_dev(w, "bf16")).data.cpu().numpy().view(np.uint16)
+    nvt, nk = -(-V // 128), K // 128
+    wp = np.zeros((nvt * 128, K), np.uint16)
+    wp[:V] = w
+    # row = vt*128 + j*16 + l16; col = c*128 + 32*kg + 8*s + e; lane = kg*16 + l16
+    want = wp.reshape(nvt, 8, 16, nk, 4, 4, 8).transpose(0, 3, 1, 5, 4, 2, 6).reshape(-1)
+    np.testing.assert_array_equal(got, want)
+
+
 def test_lmhead_ties_go_to_smallest_index():
     import tree_draft_verification_amd as tv
     from workloads import bf16_bits_from_f32
     rng = np.random.default_rng(37)
-    M, K, V = 70, 256, 3000
+    M, K, V = 70, 512, 3000
     Hi = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
     Wi = rng.integers(-2, 3, size=(V, K)).astype(np.float32)
     Wi[2500] = Wi[11]          # duplicate rows -> exact ties across workgroups
@@ -168,8 +189,10 @@ def test_lmhead_ties_go_to_smallest_index():
     h = bf16_bits_from_f32(Hi)
     w = bf16_bits_from_f32(Wi)
     exact = Hi.astype(np.int64) @ Wi.T.astype(np.int64)
-    arg = tv.tv_lmhead_argmax(to_dev(h, "bf16"), to_dev(w, "bf16")).cpu().numpy()
-    np.testing.assert_array_equal(arg, np.argmax(exact, axis=1))
+    wd = to_dev(w, "bf16")
+    for wt in (wd, tv.tv_lmhead_pack_weights(wd)):
+        arg = tv.tv_lmhead_argmax(to_dev(h, "bf16"), wt).cpu().numpy()
+        np.testing.assert_array_equal(arg, np.argmax(exact, axis=1))
 
 
 # ---------------------------------------------------------------- accept + compact

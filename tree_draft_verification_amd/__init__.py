@@ -5,7 +5,8 @@ include/treeverify.h).  Functions carry the C names; they check tensor
 shapes, pass raw device pointers and the current HIP stream, and raise
 TreeVerifyError on a negative status.  Every step of the computation runs in
 the library's HIP kernels; torch only provides device memory and streams.
-There is no CPU fallback: importing fails if the library is not built.
+There is no CPU fallback: the first call raises ImportError if the library
+is not built.
 
 One verification step (JetSpec GitHub README, "JetSpec > Overview"):
     out        = tv_tree_verify_attn(q, k_cache, v_cache, seq_lens, parent, ...)
@@ -20,14 +21,23 @@ import math
 import torch
 
 from . import _lib
-from ._lib import (TV_BF16, TV_F32, TV_MAX_NODES, TV_STATUS_BAD_LEN,  # noqa: F401
-                   TV_STATUS_BAD_PARENT, TV_STATUS_DEPTH)
+from ._lib import (TV_BF16, TV_F32, TV_LAYOUT_PACKED, TV_LAYOUT_ROWMAJOR,  # noqa: F401
+                   TV_MAX_NODES, TV_STATUS_BAD_LEN, TV_STATUS_BAD_PARENT, TV_STATUS_DEPTH)
 
-_LIB = _lib.load()
+_LIB_HANDLE = None
+
+
+def _lib_handle():
+    """The loaded library (loaded on first use; raises if it is not built)."""
+    global _LIB_HANDLE
+    if _LIB_HANDLE is None:
+        _LIB_HANDLE = _lib.load()
+    return _LIB_HANDLE
 
 __all__ = [
     "TreeVerifyError", "tv_tree_verify_attn", "tv_tree_verify_attn_workspace",
-    "tv_lmhead_argmax", "tv_lmhead_argmax_workspace", "tv_tree_accept",
+    "tv_lmhead_argmax", "tv_lmhead_argmax_workspace", "tv_lmhead_packed_bytes",
+    "tv_lmhead_pack_weights", "PackedWeights", "tv_tree_accept",
     "tv_kv_compact", "tv_status_string", "tv_abi_version", "library_path",
 ]
 
@@ -43,11 +53,11 @@ def library_path() -> str:
 
 
 def tv_status_string(status: int) -> str:
-    return _LIB.tv_status_string(int(status)).decode()
+    return _lib_handle().tv_status_string(int(status)).decode()
 
 
 def tv_abi_version() -> int:
-    return int(_LIB.tv_abi_version())
+    return int(_lib_handle().tv_abi_version())
 
 
 def _check(fn: str, status: int) -> None:
@@ -103,7 +113,7 @@ def _cached_workspace(kind: str, nbytes: int, dev: torch.device) -> torch.Tensor
 # ---------------------------------------------------------------- attention
 
 def tv_tree_verify_attn_workspace(B, N, Hq, Hkv, D, max_seq_len, dtype=TV_BF16) -> int:
-    return int(_LIB.tv_tree_verify_attn_workspace(B, N, Hq, Hkv, D, max_seq_len, dtype))
+    return int(_lib_handle().tv_tree_verify_attn_workspace(B, N, Hq, Hkv, D, max_seq_len, dtype))
 
 
 def tv_tree_verify_attn(q, k_cache, v_cache, seq_lens, parent, out=None, *,
@@ -130,7 +140,7 @@ def tv_tree_verify_attn(q, k_cache, v_cache, seq_lens, parent, out=None, *,
     if workspace is None and need > 0:
         workspace = _cached_workspace("attn", need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _LIB.tv_tree_verify_attn(
+    st = _lib_handle().tv_tree_verify_attn(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(parent), _ptr(out),
         B, N, Hq, Hkv, D, Lcap, int(max_seq_len), float(scale), dt,
         _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(q.device))
@@ -140,13 +150,44 @@ def tv_tree_verify_attn(q, k_cache, v_cache, seq_lens, parent, out=None, *,
 
 # ---------------------------------------------------------------- LM head
 
+class PackedWeights:
+    """A vocabulary projection repacked by tv_lmhead_pack_weights.
+
+    Holds the packed device buffer and the original shape; pass it to
+    tv_lmhead_argmax in place of the [V, K] tensor.
+    """
+
+    def __init__(self, data: torch.Tensor, V: int, K: int, dtype: torch.dtype):
+        self.data, self.V, self.K, self.dtype = data, V, K, dtype
+        self.shape = (V, K)
+        self.device = data.device
+
+
 def tv_lmhead_argmax_workspace(M, K, V, dtype=TV_BF16) -> int:
-    return int(_LIB.tv_lmhead_argmax_workspace(M, K, V, dtype))
+    return int(_lib_handle().tv_lmhead_argmax_workspace(M, K, V, dtype))
+
+
+def tv_lmhead_packed_bytes(V, K, dtype=TV_BF16) -> int:
+    return int(_lib_handle().tv_lmhead_packed_bytes(V, K, dtype))
+
+
+def tv_lmhead_pack_weights(w: torch.Tensor) -> PackedWeights:
+    """Repack a [V, K] bf16 vocabulary projection once for the fast layout."""
+    V, K = w.shape
+    dt = _dtype_code(w)
+    nbytes = tv_lmhead_packed_bytes(V, K, dt)
+    if nbytes == 0:
+        raise TreeVerifyError("tv_lmhead_pack_weights", _lib.TV_ENOTSUP)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    st = _lib_handle().tv_lmhead_pack_weights(_ptr(w), _ptr(out), V, K, dt, _stream(w.device))
+    _check("tv_lmhead_pack_weights", st)
+    return PackedWeights(out, V, K, w.dtype)
 
 
 def tv_lmhead_argmax(hidden, w, argmax=None, logits=None, *,
                      workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """argmax[r] = argmax_v sum_k hidden[r,k] w[v,k].  hidden [M,K]; w [V,K].
+    """argmax[r] = argmax_v sum_k hidden[r,k] w[v,k].  hidden [M,K]; w [V,K]
+    (a tensor, row-major) or a PackedWeights.
 
     A caller-supplied workspace must be zero-filled before its first use.
     """
@@ -155,6 +196,10 @@ def tv_lmhead_argmax(hidden, w, argmax=None, logits=None, *,
     if Kw != K or w.dtype != hidden.dtype:
         raise ValueError("hidden and w disagree in width or dtype")
     dt = _dtype_code(hidden)
+    if isinstance(w, PackedWeights):
+        layout, wptr = TV_LAYOUT_PACKED, _ptr(w.data)
+    else:
+        layout, wptr = TV_LAYOUT_ROWMAJOR, _ptr(w)
     if argmax is None:
         argmax = torch.empty(M, dtype=torch.int32, device=hidden.device)
     _i32(argmax, (M,), "argmax")
@@ -164,8 +209,8 @@ def tv_lmhead_argmax(hidden, w, argmax=None, logits=None, *,
     if workspace is None:
         workspace = _cached_workspace("lmhead", need, hidden.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = _LIB.tv_lmhead_argmax(_ptr(hidden), _ptr(w), _ptr(argmax), _ptr(logits), M, K, V, dt,
-                               _ptr(workspace), ws_bytes, _stream(hidden.device))
+    st = _lib_handle().tv_lmhead_argmax(_ptr(hidden), wptr, _ptr(argmax), _ptr(logits), M, K, V, dt,
+                               layout, _ptr(workspace), ws_bytes, _stream(hidden.device))
     _check("tv_lmhead_argmax", st)
     return argmax
 
@@ -190,7 +235,7 @@ def tv_tree_accept(parent, draft_tokens, target_tokens, P: int = 32, *, path=Non
     _i32(path, (B, P), "path")
     _i32(path_len, (B,), "path_len")
     _i32(bonus, (B,), "bonus")
-    st = _LIB.tv_tree_accept(_ptr(parent), _ptr(draft_tokens), _ptr(target_tokens),
+    st = _lib_handle().tv_tree_accept(_ptr(parent), _ptr(draft_tokens), _ptr(target_tokens),
                              _ptr(path), _ptr(path_len), _ptr(bonus), B, N, P,
                              _ptr(dev_status), _stream(dev))
     _check("tv_tree_accept", st)
@@ -209,6 +254,6 @@ def tv_kv_compact(k_cache, v_cache, seq_lens, path, path_len) -> None:
     P = path.shape[1]
     _i32(path, (B, P), "path")
     _i32(path_len, (B,), "path_len")
-    st = _LIB.tv_kv_compact(_ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(path),
+    st = _lib_handle().tv_kv_compact(_ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(path),
                             _ptr(path_len), B, Hkv, D, Lcap, P, dt, _stream(k_cache.device))
     _check("tv_kv_compact", st)

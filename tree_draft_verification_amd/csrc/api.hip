@@ -29,7 +29,7 @@ const char* tv_status_string(int status) {
   switch (status) {
     case TV_OK: return "ok";
     case TV_EINVAL: return "invalid argument (shape, size or null pointer)";
-    case TV_ENOTSUP: return "unsupported configuration (head dim, dtype, node count or k)";
+    case TV_ENOTSUP: return "unsupported configuration (head dim, dtype, layout, node count or width)";
     case TV_EWORKSPACE: return "workspace missing or too small";
     case TV_EHIP: return g_hip_msg[0] ? g_hip_msg : "HIP launch failed";
     default: return "unknown status";
@@ -72,18 +72,34 @@ size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype) {
   return tv::lmhead_ws_bytes(M, K, V, dtype);
 }
 
+size_t tv_lmhead_packed_bytes(int V, int K, int dtype) {
+  if (V < 1 || K < 1 || dtype != TV_BF16 || K % 256) return 0;
+  return tv::lmhead_packed_bytes(V, K);
+}
+
+int tv_lmhead_pack_weights(const void* w, void* w_packed, int V, int K, int dtype,
+                           void* stream) {
+  if (!w || !w_packed || w == w_packed) return TV_EINVAL;
+  if (V < 1 || K < 1) return TV_EINVAL;
+  if (dtype != TV_BF16 || K % 256) return TV_ENOTSUP;
+  return hip_status(tv::launch_lmhead_pack(w, w_packed, V, K, static_cast<hipStream_t>(stream)));
+}
+
 int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax, float* logits, int M,
-                     int K, int V, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+                     int K, int V, int dtype, int w_layout, void* workspace, size_t ws_bytes,
+                     void* stream) {
   if (!hidden || !w || !argmax) return TV_EINVAL;
   if (M < 1 || K < 1 || V < 1) return TV_EINVAL;
+  if (w_layout != TV_LAYOUT_ROWMAJOR && w_layout != TV_LAYOUT_PACKED) return TV_EINVAL;
   if (!dtype_ok(dtype)) return TV_ENOTSUP;
-  if (dtype == TV_BF16 && K % 128) return TV_ENOTSUP;
+  if (dtype == TV_BF16 && K % 256) return TV_ENOTSUP;
+  if (dtype == TV_F32 && w_layout != TV_LAYOUT_ROWMAJOR) return TV_ENOTSUP;
   const long long blocks = dtype == TV_BF16
                                ? (long long)((M + 63) / 64) * ((V + 127) / 128)
                                : (long long)((M + 15) / 16) * ((V + 255) / 256);
   if (blocks > 2147483647LL) return TV_ENOTSUP;
   if (!workspace || ws_bytes < tv::lmhead_ws_bytes(M, K, V, dtype)) return TV_EWORKSPACE;
-  return hip_status(tv::launch_lmhead_argmax(hidden, w, argmax, logits, M, K, V, dtype,
+  return hip_status(tv::launch_lmhead_argmax(hidden, w, argmax, logits, M, K, V, dtype, w_layout,
                                              workspace, static_cast<hipStream_t>(stream)));
 }
 

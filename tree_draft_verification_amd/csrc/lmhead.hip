@@ -4,32 +4,42 @@
 // README, "JetSpec > Overview"); at temperature 0 (the README's "Quick Start"
 // examples) that is the argmax of  logits[r][v] = sum_k hidden[r][k] w[v][k].
 // The logits are never written on the hot path: each workgroup reduces its
-// tile to one (value, index) key per row and folds it into a per-row 64-bit
-// atomicMax; the last workgroup to finish turns the keys into indices and
-// clears them.  Max over packed keys is order-independent, so the result is
-// deterministic, with ties going to the smallest index.
+// tile to one packed (value, index) key per row and folds it into a per-row
+// 64-bit atomic max; the last workgroup to finish turns the keys into indices
+// and clears them.  A max over packed keys does not depend on the order of
+// arrival, so the result is deterministic, with ties to the smallest index.
 //
-// bf16 kernel: a workgroup owns 128 vocabulary rows x 64 hidden-state rows.
-// Every vocabulary row is read from HBM by exactly one workgroup per 64-row
-// slice of hidden states; it goes straight from HBM into MFMA A-operand
-// registers - each lane streams 64 contiguous bytes of one row per 128-wide k
-// chunk, so four lanes cover 256 contiguous bytes - with the next chunk in
-// flight while the current one is multiplied.  The reduction index k is
-// permuted identically in both operands, which is what lets a lane's 64 bytes
-// serve four consecutive 32-wide MFMA k-steps.  The hidden-state slice, shared
-// by all four wavefronts, is staged through double-buffered LDS.  Workgroups
-// that share a vocabulary tile (different hidden-state slices) get adjacent
-// logical ids, which the remap places on one die so the tile is read from HBM
-// once and served from that die's L2 afterwards.
+// bf16 streaming kernel (few hidden-state rows: the step is bound by reading
+// the vocabulary matrix once from HBM):
+//   * A workgroup owns 128 vocabulary rows x 64 hidden-state rows; each of
+//     its 4 wavefronts owns 32 vocabulary rows (two 16-row MFMA blocks).
+//   * The vocabulary rows go straight from HBM into MFMA A-operand registers
+//     through a two-deep register ring (chunk c+2 is in flight while chunk c
+//     is multiplied).  Every load is unconditional (addresses are clamped and
+//     out-of-range rows are dropped in the epilogue): a lane-dependent branch
+//     around a load would make the compiler wait for every outstanding load
+//     at the next use, which serialises the stream.
+//   * The reduction index k is permuted identically in both operands, so a
+//     lane's 64 contiguous bytes of one row serve four 32-wide k-steps.
+//   * The 64 hidden-state rows, shared by the 4 wavefronts, are staged
+//     through double-buffered LDS, one 128-wide k chunk at a time.
+//   * Packed vocabulary layout (tv_lmhead_pack_weights): the 4 KB that one
+//     wavefront consumes for one 16-row block and one k chunk are stored
+//     contiguously in lane order, and a workgroup's whole tile is contiguous,
+//     so every load instruction reads 1 KB of consecutive bytes; the
+//     row-major layout reads 16 rows x 64 bytes per instruction instead.
+//   * Workgroups that share a vocabulary tile (different 64-row slices of
+//     hidden states) get adjacent logical ids, which the remap places on one
+//     die so that the tile comes from HBM once and from that die's L2 after.
 #include "tv_internal.h"
 
 namespace tv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVT = 128;   // vocabulary rows per workgroup (32 per wavefront)
-constexpr int kMT = 64;    // hidden-state rows per workgroup
-constexpr int kKC = 128;   // k per pipeline stage
+constexpr int kVT = 128;        // vocabulary rows per workgroup (32 per wavefront)
+constexpr int kMT = 64;         // hidden-state rows per workgroup
+constexpr int kKC = 128;        // k per pipeline stage
 constexpr int kHRow = kKC + 8;  // LDS row of the hidden-state slice (bf16)
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int off) {
@@ -39,29 +49,44 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x,
 }
 
 // Fold this workgroup's per-row keys into the global keys; the last
-// workgroup converts them to indices and leaves the workspace zeroed.
+// workgroup converts them to indices and leaves the workspace zeroed.  The
+// atomics return their old value and that value is consumed before the
+// barrier, so every key update of a workgroup has completed before its
+// counter increment is issued; no device-wide fence (and no L2 write-back)
+// is needed.
 __device__ __forceinline__ void argmax_commit(unsigned long long* keys, unsigned* counter,
-                                              int32_t* argmax, int M, int total_blocks,
-                                              int m0, int mt, const unsigned long long* s_rowkey) {
-  const int tid = threadIdx.x;
-  if (tid < mt && m0 + tid < M) atomicMax(&keys[m0 + tid], s_rowkey[tid]);
-  __threadfence();
-  __syncthreads();
+                                              int32_t* argmax, int M, int total_blocks, int m0,
+                                              int mt, const unsigned long long* s_rowkey) {
   __shared__ int s_last;
+  const int tid = threadIdx.x;
+  if (tid < mt && m0 + tid < M) {
+    const unsigned long long old = __hip_atomic_fetch_max(
+        &keys[m0 + tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == 1ull) s_last = 0;  // never true (keys exceed 2^32); forces the wait
+  }
+  __syncthreads();
   if (tid == 0) {
-    const unsigned prev = atomicAdd(counter, 1u);
-    s_last = (prev == (unsigned)total_blocks - 1u);
+    const unsigned prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)total_blocks - 1u;
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   for (int m = tid; m < M; m += blockDim.x) {
-    const unsigned long long k = atomicExch(&keys[m], 0ull);
+    const unsigned long long k =
+        __hip_atomic_exchange(&keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     argmax[m] = (int32_t)(~(uint32_t)(k & 0xffffffffull));
   }
-  if (tid == 0) atomicExch(counter, 0u);
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Address of piece s (16 bytes) of lane `lane` of 16-row block j of tile vt,
+// k chunk c, in the packed layout (bf16 elements).
+__device__ __forceinline__ size_t packed_offset(int vt, int c, int nk, int j, int s, int lane) {
+  return (((((size_t)vt * nk + c) * 8 + j) * 4 + s) * 64 + lane) * 8;
+}
+
+template <bool PACKED>
 __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
     const bf16_t* __restrict__ H, const bf16_t* __restrict__ W, int32_t* __restrict__ argmax,
     float* __restrict__ logits, unsigned long long* __restrict__ keys,
@@ -81,41 +106,44 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
   const int vt = lid / nmt;
   const int m0 = mt * kMT;
   const int v0 = vt * kVT;
+  const int nk = K / kKC;
 
-  // this lane's two vocabulary rows (one per 16-row block)
+  // W source of this lane (clamped rows in the row-major layout; the packed
+  // layout is zero-padded to whole tiles)
   const bf16_t* wrow[2];
-  bool wok[2];
 #pragma unroll
   for (int vb = 0; vb < 2; ++vb) {
     const int v = v0 + wave * 32 + vb * 16 + l16;
-    wok[vb] = v < V;
-    wrow[vb] = W + (size_t)(wok[vb] ? v : 0) * K + 32 * kg;
+    wrow[vb] = W + (size_t)(v < V ? v : V - 1) * K + 32 * kg;
   }
+  auto wload = [&](int c, int vb, int s) -> uint4 {
+    if constexpr (PACKED)
+      return *reinterpret_cast<const uint4*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane));
+    else
+      return *reinterpret_cast<const uint4*>(wrow[vb] + c * kKC + 8 * s);
+  };
   // this thread's four 16-byte pieces of each hidden-state stage
   const bf16_t* hsrc[4];
-  bool hok[4];
   int hdst[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + i * kThreads;
-    const int r = c / (kKC / 8);
-    const int x = c - r * (kKC / 8);
-    hok[i] = m0 + r < M;
-    hsrc[i] = H + (size_t)(hok[i] ? m0 + r : 0) * K + x * 8;
+    const int r = c >> 4;
+    const int x = c & 15;
+    hsrc[i] = H + (size_t)(m0 + r < M ? m0 + r : M - 1) * K + x * 8;
     hdst[i] = r * kHRow + x * 8;
   }
 
-  const int nk = K / kKC;
-  uint4 wcur[2][4], wnxt[2][4], hreg[4];
-  const uint4 z = make_uint4(0, 0, 0, 0);
-
+  uint4 wb[2][2][4];  // [ring slot][16-row block][piece]
+  uint4 hreg[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hreg[i] = hok[i] ? *reinterpret_cast<const uint4*>(hsrc[i]) : z;
+  for (int d = 0; d < 2; ++d)
 #pragma unroll
-  for (int vb = 0; vb < 2; ++vb)
+    for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      wcur[vb][s] = wok[vb] ? *reinterpret_cast<const uint4*>(wrow[vb] + 8 * s) : z;
+      for (int s = 0; s < 4; ++s) wb[d][vb][s] = wload(min(d, nk - 1), vb, s);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sH[0][hdst[i]]) = hreg[i];
   __syncthreads();
@@ -126,44 +154,38 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[vb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = 0; c < nk; ++c) {
-    const bool more = c + 1 < nk;
-    if (more) {
-      const int ko = (c + 1) * kKC;
+  // nk is even (K is a multiple of 256): two chunks per trip keep the ring
+  // slot and the LDS buffer compile-time constants.
+  for (int c0 = 0; c0 < nk; c0 += 2) {
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
+    for (int u = 0; u < 2; ++u) {
+      const int c = c0 + u;
+      const int ch = min(c + 1, nk - 1);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          wnxt[vb][s] = wok[vb] ? *reinterpret_cast<const uint4*>(wrow[vb] + ko + 8 * s) : z;
+      for (int i = 0; i < 4; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i] + ch * kKC);
+      const bf16_t* sh = sH[u];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hreg[i] = hok[i] ? *reinterpret_cast<const uint4*>(hsrc[i] + ko) : z;
-    }
-    const bf16_t* sh = sH[c & 1];
+      for (int s = 0; s < 4; ++s) {
+        Frag8 hf[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      Frag8 hf[4];
+        for (int mb = 0; mb < 4; ++mb)
+          hf[mb].u = *reinterpret_cast<const uint4*>(&sh[(mb * 16 + l16) * kHRow + 32 * kg + 8 * s]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        hf[mb].u = *reinterpret_cast<const uint4*>(&sh[(mb * 16 + l16) * kHRow + 32 * kg + 8 * s]);
+        for (int vb = 0; vb < 2; ++vb) {
+          Frag8 wf;
+          wf.u = wb[u][vb][s];
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        Frag8 wf;
-        wf.u = wcur[vb][s];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[vb][mb] = mfma16x16x32(wf.v, hf[mb].v, acc[vb][mb]);
+          for (int mb = 0; mb < 4; ++mb) acc[vb][mb] = mfma16x16x32(wf.v, hf[mb].v, acc[vb][mb]);
+        }
       }
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sH[(c + 1) & 1][hdst[i]]) = hreg[i];
-    }
-    __syncthreads();
-    if (more) {
+      const int cw = min(c + 2, nk - 1);
 #pragma unroll
       for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) wcur[vb][s] = wnxt[vb][s];
+        for (int s = 0; s < 4; ++s) wb[u][vb][s] = wload(cw, vb, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sH[u ^ 1][hdst[i]]) = hreg[i];
+      __syncthreads();
     }
   }
 
@@ -210,6 +232,31 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
   }
   __syncthreads();
   argmax_commit(keys, counter, argmax, M, total_blocks, m0, kMT, s_rowkey);
+}
+
+// Row-major [V][K] -> packed layout; one thread per 16-byte packed piece,
+// rows past V written as zeros.
+__global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ W,
+                                                   bf16_t* __restrict__ P, int K, int V,
+                                                   size_t pieces) {
+  const int nk = K / kKC;
+  for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < pieces;
+       p += (size_t)gridDim.x * blockDim.x) {
+    size_t t = p;
+    const int lane = (int)(t % 64);
+    t /= 64;
+    const int s = (int)(t % 4);
+    t /= 4;
+    const int j = (int)(t % 8);
+    t /= 8;
+    const int c = (int)(t % nk);
+    const size_t vt = t / nk;
+    const size_t row = vt * kVT + j * 16 + (lane & 15);
+    const int col = c * kKC + 32 * (lane >> 4) + 8 * s;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (row < (size_t)V) val = *reinterpret_cast<const uint4*>(W + row * K + col);
+    reinterpret_cast<uint4*>(P)[p] = val;
+  }
 }
 
 // fp32 path: one thread per vocabulary row, 16 hidden-state rows per
@@ -279,9 +326,20 @@ size_t lmhead_ws_bytes(int M, int /*K*/, int /*V*/, int /*dtype*/) {
   return ((size_t)M * 8 + 255) / 256 * 256 + 256;
 }
 
+size_t lmhead_packed_bytes(int V, int K) {
+  return (size_t)((V + kVT - 1) / kVT) * kVT * (size_t)K * sizeof(bf16_t);
+}
+
+hipError_t launch_lmhead_pack(const void* w, void* packed, int V, int K, hipStream_t stream) {
+  const size_t pieces = lmhead_packed_bytes(V, K) / 16;
+  hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(w), static_cast<bf16_t*>(packed), K, V, pieces);
+  return hipGetLastError();
+}
+
 hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
-                                float* logits, int M, int K, int V, int dtype, void* ws,
-                                hipStream_t stream) {
+                                float* logits, int M, int K, int V, int dtype, int w_layout,
+                                void* ws, hipStream_t stream) {
   unsigned long long* keys = static_cast<unsigned long long*>(ws);
   unsigned* counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) +
                                                   ((size_t)M * 8 + 255) / 256 * 256);
@@ -297,9 +355,14 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
   const int nmt = (M + kMT - 1) / kMT;
   const int nvt = (V + kVT - 1) / kVT;
   const int total = nmt * nvt;
-  hipLaunchKernelGGL(lmhead_bf16_kernel, dim3(total), dim3(kThreads), 0, stream,
-                     static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w), argmax,
-                     logits, keys, counter, M, K, V, nmt, total);
+  const bf16_t* h = static_cast<const bf16_t*>(hidden);
+  const bf16_t* wv = static_cast<const bf16_t*>(w);
+  if (w_layout == TV_LAYOUT_PACKED)
+    hipLaunchKernelGGL(lmhead_bf16_kernel<true>, dim3(total), dim3(kThreads), 0, stream, h, wv,
+                       argmax, logits, keys, counter, M, K, V, nmt, total);
+  else
+    hipLaunchKernelGGL(lmhead_bf16_kernel<false>, dim3(total), dim3(kThreads), 0, stream, h, wv,
+                       argmax, logits, keys, counter, M, K, V, nmt, total);
   return hipGetLastError();
 }
 

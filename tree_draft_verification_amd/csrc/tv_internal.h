@@ -89,9 +89,12 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
                             hipStream_t stream);
 
 size_t lmhead_ws_bytes(int M, int K, int V, int dtype);
+size_t lmhead_packed_bytes(int V, int K);
+
+hipError_t launch_lmhead_pack(const void* w, void* packed, int V, int K, hipStream_t stream);
 
 hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
-                                float* logits, int M, int K, int V, int dtype,
+                                float* logits, int M, int K, int V, int dtype, int w_layout,
                                 void* ws, hipStream_t stream);
 
 hipError_t launch_tree_accept(const int32_t* parent, const int32_t* draft,
