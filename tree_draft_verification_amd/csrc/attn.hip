@@ -6,43 +6,49 @@
 // its own root path (rows L_b+j, j an ancestor of i or i itself):
 //     out[b][i][h] = softmax(scale * q K_vis^T) V_vis,   KV head = h / G.
 //
-// bf16 kernel (gfx950 matrix cores):
-//   * A workgroup (4 wavefronts) owns 128 query rows of one (sequence, KV
-//     head).  Row r is node r / G, head r % G of the group, so the G heads of
-//     one node - which share every key and the whole mask - are adjacent and
-//     the key/value tiles staged in LDS are shared by all 128 rows.
-//   * Per 64-key tile: S^T = K Q^T on 16x16x32 bf16 MFMA (K rows from LDS,
-//     Q^T fragments held in registers for the whole loop), then an online
-//     softmax in the exp2 domain, then O^T += V^T P^T on MFMA.  Computing the
-//     transposed products leaves each lane with one query column in both
-//     results, so the softmax state of a query never leaves its lane, and the
-//     probabilities feed the second product straight from registers (the key
-//     order inside the 32-wide k-step is permuted identically in V^T and
-//     P^T).  V is stored transposed in LDS for that product.
-//   * The mask is one 64-bit ancestor word per (node, 64-key tree tile),
-//     built in LDS at kernel start by walking parent pointers from each node
-//     of the block (TV_STATUS_BAD_PARENT on a malformed tree).  Tree tiles
-//     past the block's last node are skipped: a node only sees lower indices.
-//   * Long prefixes are split across workgroups (split-KV).  Each split writes
-//     fp32 (max, sum, unnormalised output) partials and a combine kernel
-//     merges them; with one split the kernel writes the output directly.
-//     The tree keys are handled by the last split.
-//   * Workgroup ids are remapped so that the query blocks and splits that read
-//     the same key/value rows run on the same die (shared L2).
+// bf16 kernel (gfx950 matrix cores), attn_bf16_kernel<D, QBW, NW>:
+//   * A workgroup of NW wavefronts owns NW*QBW*16 query rows of one
+//     (sequence, KV head); row r is node r / G, head r % G of the group, so
+//     the G heads of a node - which share every key and the whole mask - are
+//     adjacent, and each 64-key K/V tile staged in LDS serves every row.
+//   * Per tile: S^T = K Q^T on 16x16x32 bf16 MFMA (Q^T fragments stay in
+//     registers), online softmax, O^T += V^T P^T.  With the transposed
+//     products each lane owns one query column in both results, so the
+//     softmax state never moves between lanes and the probabilities feed the
+//     second product straight from registers (the key order inside a 32-wide
+//     k-step is permuted identically in V^T and P^T).  V is transposed on its
+//     way into LDS.
+//   * A tile's loads are issued back to back and are unconditional (rows
+//     past the valid range are clamped to a valid row and masked out of the
+//     scores), so they are all in flight at once; they are not held in
+//     registers across the products, which keeps the kernel at two or more
+//     workgroups per CU so that one workgroup's loads overlap another's
+//     products.
+//   * Softmax in the exp2 domain: one FMA folds the scale and the running
+//     max, then v_exp_f32; probabilities go to bf16 with v_cvt_pk_bf16_f32.
+//     The running reference max moves only when a wavefront sees a score more
+//     than 2^8 above it (rescaling O and the sum); until then probabilities up
+//     to 2^8 accumulate exactly as they would after a rescale.
+//   * Masking runs only on tree tiles and partial tiles.  The mask is one
+//     64-bit ancestor word per (node, 64-key tree tile), built in LDS by
+//     walking parent pointers (TV_STATUS_BAD_PARENT on a malformed tree);
+//     tree tiles that no node of the block can see are skipped.
+//   * Long prefixes can be split across workgroups (split-KV): each writes
+//     fp32 (reference max, sum, unnormalised output) partials and a combine
+//     kernel merges them; the tree keys go to the last split.
+//   * Workgroup ids are remapped so that the blocks reading the same K/V rows
+//     run on the same die (shared L2).
 // fp32 kernel: a plain VALU kernel for small fp32 problems.
 #include "tv_internal.h"
 
 namespace tv {
 namespace {
 
-constexpr int kKT = 64;          // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 32;  // two 16-query MFMA column blocks
-constexpr int kRowsPerBlock = kWaves * kRowsPerWave;  // 128
-constexpr int kKPad = 8;         // bf16 padding of a K row in LDS
-constexpr int kVPad = 4;         // bf16 padding of a V^T row in LDS
+constexpr int kKT = 64;     // keys per tile
+constexpr int kKPad = 8;    // bf16 padding of a K row in LDS
+constexpr int kVPad = 4;    // bf16 padding of a V^T row in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;  // rescale when a score exceeds the reference by 2^8
 
 struct AttnArgs {
   const bf16_t* q;
@@ -51,12 +57,12 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* parent;
   bf16_t* out;
-  float* part_o;   // [B*Hkv][nqblk*128][nsplit][D] fp32
-  float* part_ml;  // [B*Hkv][nqblk*128][nsplit][2] fp32
+  float* part_o;   // [B*Hkv][nqblk*rows][nsplit][D] fp32
+  float* part_ml;  // [B*Hkv][nqblk*rows][nsplit][2] fp32
   int32_t* dev_status;
   int B, N, Hq, Hkv, G, Lcap, max_seq_len;
+  int rows;        // query rows per workgroup
   int nqblk, nsplit, chunk_len, total_blocks;
-  int anc_nodes;   // node slots of the ancestor table in LDS
   int anc_words;   // ceil(N / 64)
   float scale_log2;  // scale * log2(e)
 };
@@ -65,16 +71,49 @@ __device__ __forceinline__ void flag(int32_t* st, int b, int f) {
   if (st) atomicOr(&st[b], f);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
+// Reductions across the four 16-lane groups of a wavefront (lanes l, l^16,
+// l^32, l^48) with the gfx950 row/half swaps: each swap returns both
+// operands exchanged, so combining its two results pairs every lane with
+// its partner without a trip through LDS.
+__device__ __forceinline__ float max_across_groups(float x) {
+  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_groups(float x) {
+  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int D, int QBW, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bf16_kernel(AttnArgs a) {
+  constexpr int kThreads = NW * 64;
+  constexpr int kRows = NW * QBW * 16;
   constexpr int DS = D / 32;  // k-steps of the QK^T product
   constexpr int DB = D / 16;  // 16-row output blocks of the PV product
   constexpr int KROW = D + kKPad;
   constexpr int VROW = kKT + kVPad;
+  constexpr int KP_TOTAL = kKT * D / 8;           // 16-byte pieces of a K tile
+  constexpr int KP = (KP_TOTAL + kThreads - 1) / kThreads;
+  constexpr int VI_TOTAL = (kKT / 4) * (D / 8);   // 4-key x 8-dim items of a V tile
+  constexpr int VI = (VI_TOTAL + kThreads - 1) / kThreads;
+  constexpr int kMaxAncNodes = kRows + 2;
   __shared__ __attribute__((aligned(16))) bf16_t sK[kKT * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t sVt[D * VROW];
   __shared__ int16_t sPar[TV_MAX_NODES];
-  extern __shared__ unsigned long long sAnc[];  // [anc_nodes][anc_words]
+  __shared__ unsigned long long sAnc[kMaxAncNodes * (TV_MAX_NODES / 64)];
+  __shared__ unsigned sTreeMask;
+  __shared__ int8_t sTreeList[TV_MAX_NODES / 64];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -98,14 +137,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     if (tid == 0) flag(a.dev_status, b, TV_STATUS_BAD_LEN);
     return;
   }
-  const int row0 = qblk * kRowsPerBlock;
+  const int row0 = qblk * kRows;
   const int node_lo = row0 / G;
-  const int node_hi = (min(R, row0 + kRowsPerBlock) - 1) / G;
+  const int node_hi = (min(R, row0 + kRows) - 1) / G;
   const bool do_tree = (split == a.nsplit - 1);
   const int c0 = split * a.chunk_len;
   const int c1 = min(c0 + a.chunk_len, L);
+  const int W = a.anc_words;
 
-  // ---- ancestor words of the block's nodes (tree split only)
+  // ---- ancestor words of the block's nodes and the tree tiles they touch
+  int n_tree = 0;
   if (do_tree) {
     const int32_t* par = a.parent + (size_t)b * N;
     int bad = 0;
@@ -116,29 +157,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       sPar[i] = (int16_t)(ok ? p : -1);
     }
     const int nn = node_hi - node_lo + 1;
-    for (int x = tid; x < nn * a.anc_words; x += kThreads) sAnc[x] = 0ull;
+    for (int x = tid; x < nn * W; x += kThreads) sAnc[x] = 0ull;
+    if (tid == 0) sTreeMask = 0u;
     __syncthreads();
     for (int n = tid; n < nn; n += kThreads) {
-      unsigned long long* w = sAnc + n * a.anc_words;
+      unsigned long long* w = sAnc + n * W;
+      unsigned used = 0u;
       int j = node_lo + n;
       while (j >= 0) {  // parent[j] < j, so this ends within j + 1 steps
         w[j >> 6] |= 1ull << (j & 63);
+        used |= 1u << (j >> 6);
         j = (j == 0) ? -1 : sPar[j];
       }
+      atomicOr(&sTreeMask, used);
     }
     if (bad) flag(a.dev_status, b, TV_STATUS_BAD_PARENT);
+    __syncthreads();
+    const unsigned mask = sTreeMask;
+    n_tree = __popc(mask);
+    if (tid == 0) {
+      int k = 0;
+      for (int tt = 0; tt < W; ++tt)
+        if (mask & (1u << tt)) sTreeList[k++] = (int8_t)tt;
+    }
+    // (published to the other threads by the first barrier of the tile loop)
   }
 
-  // ---- Q^T fragments of this lane's two query columns
+  // ---- Q^T fragments of this lane's query columns
   const size_t kv_plane = ((size_t)b * a.Hkv + g) * (size_t)a.Lcap * D;
   const bf16_t* kp = a.k + kv_plane;
   const bf16_t* vp = a.v + kv_plane;
-  bf16x8_t qf[2][DS];
-  int qnode[2];
-  bool qvalid[2];
+  bf16x8_t qf[QBW][DS];
+  int qnode[QBW];
+  bool qvalid[QBW];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = row0 + wave * kRowsPerWave + qb * 16 + l16;
+  for (int qb = 0; qb < QBW; ++qb) {
+    const int row = row0 + wave * QBW * 16 + qb * 16 + l16;
     qvalid[qb] = row < R;
     const int node = qvalid[qb] ? row / G : node_hi;
     const int hh = qvalid[qb] ? row - node * G : 0;
@@ -147,125 +201,163 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       Frag8 f;
-      f.u = qvalid[qb] ? *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * kg)
-                       : make_uint4(0, 0, 0, 0);
+      f.u = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * kg);
       qf[qb][s] = f.v;
     }
   }
 
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  f32x4_t o[2][DB];
+  float m_ref[QBW], l_run[QBW];
+  f32x4_t o[QBW][DB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QBW; ++qb) {
+    m_ref[qb] = -INFINITY;
+    l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[qb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int n_pre = (c1 > c0) ? (c1 - c0 + kKT - 1) / kKT : 0;
-  const int n_tree = do_tree ? (node_hi / kKT + 1) : 0;
+  const int n_tiles = n_pre + n_tree;
 
-  for (int it = 0; it < n_pre + n_tree; ++it) {
-    const bool tree = it >= n_pre;
-    const int tt = it - n_pre;
-    const int krow0 = tree ? L + tt * kKT : c0 + it * kKT;
-    const int nvalid = tree ? min(kKT, N - tt * kKT) : min(kKT, c1 - krow0);
+  // Tile descriptor: first cache row and number of valid keys.
+  auto tile_rows = [&](int it, int& krow0, int& nvalid, int& tt) {
+    if (it < n_pre) {
+      krow0 = c0 + it * kKT;
+      nvalid = min(kKT, c1 - krow0);
+      tt = -1;
+    } else {
+      tt = sTreeList[it - n_pre];
+      krow0 = L + tt * kKT;
+      nvalid = min(kKT, N - tt * kKT);
+    }
+  };
 
-    __syncthreads();  // previous tile fully consumed (and ancestor table built)
-    // K tile: rows krow0.. are contiguous in the plane; 16-byte pieces.
-    for (int c = tid; c < kKT * (D / 8); c += kThreads) {
+  // Register staging of one tile: K pieces and V 4-key items.
+  uint4 kreg[KP];
+  uint4 vreg[VI][4];
+  auto load_tile = [&](int krow0, int nvalid) {
+    const int last = krow0 + nvalid - 1;
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int c = min(tid + i * kThreads, KP_TOTAL - 1);
       const int r = c / (D / 8);
       const int x = c - r * (D / 8);
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (r < nvalid) val = *reinterpret_cast<const uint4*>(kp + (size_t)(krow0 + r) * D + x * 8);
-      *reinterpret_cast<uint4*>(&sK[r * KROW + x * 8]) = val;
+      kreg[i] = *reinterpret_cast<const uint4*>(kp + (size_t)min(krow0 + r, last) * D + x * 8);
     }
-    // V tile, transposed: a thread takes 4 keys x 8 dims and writes 8 rows
-    // of V^T with 4 keys each.
-    for (int c = tid; c < (kKT / 4) * (D / 8); c += kThreads) {
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int c = min(tid + i * kThreads, VI_TOTAL - 1);
       const int kq = c / (D / 8);
       const int x = c - kq * (D / 8);
-      uint4 rv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = kq * 4 + i;
-        rv[i] = (r < nvalid) ? *reinterpret_cast<const uint4*>(vp + (size_t)(krow0 + r) * D + x * 8)
-                             : make_uint4(0, 0, 0, 0);
-      }
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&rv[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&rv[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&rv[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&rv[3]);
+      for (int e = 0; e < 4; ++e)
+        vreg[i][e] = *reinterpret_cast<const uint4*>(vp + (size_t)min(krow0 + kq * 4 + e, last) * D + x * 8);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int c = min(tid + i * kThreads, KP_TOTAL - 1);
+      const int r = c / (D / 8);
+      const int x = c - r * (D / 8);
+      *reinterpret_cast<uint4*>(&sK[r * KROW + x * 8]) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int c = min(tid + i * kThreads, VI_TOTAL - 1);
+      const int kq = c / (D / 8);
+      const int x = c - kq * (D / 8);
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sh = (e & 1) * 16;
-        const uint32_t a0 = (w0[e >> 1] >> sh) & 0xffffu, a1 = (w1[e >> 1] >> sh) & 0xffffu;
-        const uint32_t a2 = (w2[e >> 1] >> sh) & 0xffffu, a3 = (w3[e >> 1] >> sh) & 0xffffu;
         uint2 pk;
-        pk.x = a0 | (a1 << 16);
-        pk.y = a2 | (a3 << 16);
+        pk.x = ((w0[e >> 1] >> sh) & 0xffffu) | (((w1[e >> 1] >> sh) & 0xffffu) << 16);
+        pk.y = ((w2[e >> 1] >> sh) & 0xffffu) | (((w3[e >> 1] >> sh) & 0xffffu) << 16);
         *reinterpret_cast<uint2*>(&sVt[(x * 8 + e) * VROW + kq * 4]) = pk;
       }
     }
-    __syncthreads();
+  };
+
+  for (int it = 0; it < n_tiles; ++it) {
+    int krow0, nvalid, tt;
+    __syncthreads();  // previous tile consumed (first trip: tree tile list visible)
+    tile_rows(it, krow0, nvalid, tt);
+    const bool tree = tt >= 0;
+    const bool need_mask = tree || nvalid < kKT;
+    // Load the tile and stage it in LDS.  The loads are issued back to back
+    // and are not held across the products: with two or more workgroups per
+    // CU, one workgroup's loads overlap another's products.
+    load_tile(krow0, nvalid);
+    store_tile();
+    __syncthreads();  // this tile is in LDS
 
     // S^T = K Q^T: lane holds query column l16, keys kb*16 + 4*kg + r.
-    f32x4_t s[2][4];
+    f32x4_t s[QBW][4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[0][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      s[1][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
         Frag8 kf;
         kf.u = *reinterpret_cast<const uint4*>(&sK[(kb * 16 + l16) * KROW + 32 * ks + 8 * kg]);
-        s[0][kb] = mfma16x16x32(kf.v, qf[0][ks], s[0][kb]);
-        s[1][kb] = mfma16x16x32(kf.v, qf[1][ks], s[1][kb]);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = mfma16x16x32(kf.v, qf[qb][ks], s[qb][kb]);
       }
     }
 
-    // mask, online softmax (exp2 domain), probabilities to bf16
-    Frag8 pf[2][2];
+    // mask (only where needed), then the online softmax in the exp2 domain
+    Frag8 pf[QBW][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      unsigned long long word = ~0ull;
-      if (tree) word = sAnc[(qnode[qb] - node_lo) * a.anc_words + tt];
+    for (int qb = 0; qb < QBW; ++qb) {
+      if (need_mask) {
+        const unsigned long long word =
+            tree ? sAnc[(qnode[qb] - node_lo) * W + tt] : ~0ull;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = kb * 16 + 4 * kg + r;
+            const bool vis = key < nvalid && ((word >> key) & 1ull);
+            s[qb][kb][r] = vis ? s[qb][kb][r] : -INFINITY;
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
+        tmax = fmaxf(fmaxf(fmaxf(tmax, s[qb][kb][0]), fmaxf(s[qb][kb][1], s[qb][kb][2])),
+                     s[qb][kb][3]);
+      tmax = max_across_groups(tmax);
+      const float tm = tmax * a.scale_log2;  // scale > 0, so max commutes
+      if (__any(tm > m_ref[qb] + kLazy)) {
+        const float m_new = fmaxf(m_ref[qb], tm);
+        const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
+        l_run[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kb * 16 + 4 * kg + r;
-          const bool vis = key < nvalid && ((word >> key) & 1ull);
-          const float x = vis ? s[qb][kb][r] * a.scale_log2 : -INFINITY;
-          s[qb][kb][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m_run[qb], tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[qb] - m_use);
-      m_run[qb] = m_new;
+        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
+        m_ref[qb] = m_new;
+      }
+      const float mu = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
       float psum = 0.f;
-      uint32_t pb[4][4];
+      float p[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(s[qb][kb][r] - m_use);
-          psum += p;
-          pb[kb][r] = f32_to_bf16(p);
+          p[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], a.scale_log2, -mu));
+          psum += p[kb][r];
         }
-      l_run[qb] = l_run[qb] * alpha + psum;
+      l_run[qb] += psum;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pf[qb][u].u = make_uint4(pb[2 * u][0] | (pb[2 * u][1] << 16),
-                                 pb[2 * u][2] | (pb[2 * u][3] << 16),
-                                 pb[2 * u + 1][0] | (pb[2 * u + 1][1] << 16),
-                                 pb[2 * u + 1][2] | (pb[2 * u + 1][3] << 16));
-      }
+      for (int u = 0; u < 2; ++u)
+        pf[qb][u].u = make_uint4(pack_bf16x2(p[2 * u][0], p[2 * u][1]),
+                                 pack_bf16x2(p[2 * u][2], p[2 * u][3]),
+                                 pack_bf16x2(p[2 * u + 1][0], p[2 * u + 1][1]),
+                                 pack_bf16x2(p[2 * u + 1][2], p[2 * u + 1][3]));
     }
 
     // O^T += V^T P^T; k-slot e of lane group kg is key 32u + 4kg + e (e < 4)
@@ -279,20 +371,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
         vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[0][db] = mfma16x16x32(vf.v, pf[0][u].v, o[0][db]);
-        o[1][db] = mfma16x16x32(vf.v, pf[1][u].v, o[1][db]);
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) o[qb][db] = mfma16x16x32(vf.v, pf[qb][u].v, o[qb][db]);
       }
     }
   }
 
   // ---- epilogue: lane holds O^T rows d = db*16 + 4*kg + r of its query
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float l_tot = l_run[qb];
-    l_tot += __shfl_xor(l_tot, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+  for (int qb = 0; qb < QBW; ++qb) {
+    const float l_tot = sum_across_groups(l_run[qb]);
     if (!qvalid[qb]) continue;
-    const int row = row0 + wave * kRowsPerWave + qb * 16 + l16;
+    const int row = row0 + wave * QBW * 16 + qb * 16 + l16;
     if (a.nsplit == 1) {
       const int node = qnode[qb];
       const int hh = row - node * G;
@@ -301,18 +391,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         uint2 pk;
-        pk.x = f32_to_bf16(o[qb][db][0] * inv) | (f32_to_bf16(o[qb][db][1] * inv) << 16);
-        pk.y = f32_to_bf16(o[qb][db][2] * inv) | (f32_to_bf16(o[qb][db][3] * inv) << 16);
+        pk.x = pack_bf16x2(o[qb][db][0] * inv, o[qb][db][1] * inv);
+        pk.y = pack_bf16x2(o[qb][db][2] * inv, o[qb][db][3] * inv);
         *reinterpret_cast<uint2*>(orow + db * 16 + 4 * kg) = pk;
       }
     } else {
-      const size_t prow = (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * kRowsPerBlock) + row) * a.nsplit + split;
+      const size_t prow =
+          (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * kRows) + row) * a.nsplit + split;
       float* po = a.part_o + prow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<f32x4_t*>(po + db * 16 + 4 * kg) = o[qb][db];
       if (kg == 0) {
-        a.part_ml[prow * 2 + 0] = m_run[qb];
+        a.part_ml[prow * 2 + 0] = m_ref[qb];
         a.part_ml[prow * 2 + 1] = l_tot;
       }
     }
@@ -333,14 +424,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   t /= R;
   const int g = (int)(t % a.Hkv);
   const int b = (int)(t / a.Hkv);
-  const size_t prow0 = (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * kRowsPerBlock) + row) * a.nsplit;
+  const size_t prow0 = (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * a.rows) + row) * a.nsplit;
   float mx = -INFINITY;
   for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, a.part_ml[(prow0 + s) * 2]);
   const float m_use = (mx == -INFINITY) ? 0.f : mx;
   float lsum = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < a.nsplit; ++s) {
-    const float w = exp2f(a.part_ml[(prow0 + s) * 2] - m_use);
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[(prow0 + s) * 2] - m_use);
     lsum += w * a.part_ml[(prow0 + s) * 2 + 1];
     const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + (prow0 + s) * D + d4 * 4);
     acc += w * v;
@@ -350,8 +441,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int hh = row - node * a.G;
   bf16_t* orow = a.out + (((size_t)b * a.N + node) * a.Hq + (size_t)g * a.G + hh) * D;
   uint2 pk;
-  pk.x = f32_to_bf16(acc[0] * inv) | (f32_to_bf16(acc[1] * inv) << 16);
-  pk.y = f32_to_bf16(acc[2] * inv) | (f32_to_bf16(acc[3] * inv) << 16);
+  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
   *reinterpret_cast<uint2*>(orow + d4 * 4) = pk;
 }
 
@@ -442,22 +533,52 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
   }
 }
 
+// Variant table: (query rows per wavefront / 16, wavefronts per workgroup).
+template <int D>
+hipError_t launch_bf16(const AttnArgs& a, int qbw, int nw, hipStream_t stream) {
+  const dim3 grid(a.total_blocks);
+  if (qbw == 2 && nw == 4)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4>), grid, dim3(256), 0, stream, a);
+  else if (qbw == 1 && nw == 4)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 2>), grid, dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dtype) {
   AttnPlan p{};
   const int G = Hq / Hkv;
-  const int R = N * G;
-  p.nqblk = (R + kRowsPerBlock - 1) / kRowsPerBlock;
-  p.nsplit = 1;
+  const long R = (long)N * G;
   const int ntiles = (max_seq_len + kKT - 1) / kKT;
+  const long target = 512;  // about two workgroups per CU
+  // Query rows per workgroup and prefix splits.
+  //  * Long prefixes (>= 32 tiles) keep 128-row blocks, where each K/V tile
+  //    serves the most rows, and split the prefix (>= 8 tiles per split)
+  //    until about two workgroups per CU exist.
+  //  * Short prefixes use 64-row blocks and splits of >= 4 tiles, aiming at
+  //    one workgroup per CU: there the cost is the latency of each tile, and
+  //    a finer split would write more partial results than it reads.
+  p.qbw = 2;
+  p.nw = 4;
+  p.rows = 128;
+  int min_tiles = 8;
+  long want_blocks = target;
+  if (dtype == TV_BF16 && ntiles < 32) {
+    p.qbw = 1, p.nw = 4, p.rows = 64;
+    min_tiles = 4;
+    want_blocks = target / 2;
+  }
+  p.nqblk = (int)((R + p.rows - 1) / p.rows);
+  p.nsplit = 1;
   p.chunk_len = kKT * (ntiles > 0 ? ntiles : 1);
   if (dtype == TV_BF16 && ntiles > 1) {
     const long base = (long)B * Hkv * p.nqblk;
-    const long target = 512;  // two workgroups on each of the 256 CUs
-    if (base < target) {
-      long want = (target + base - 1) / base;
-      long cap = ntiles / 2;  // at least two tiles per split
+    if (base < want_blocks) {
+      long want = (want_blocks + base - 1) / base;
+      long cap = ntiles / min_tiles;
       if (cap < 1) cap = 1;
       if (want > cap) want = cap;
       const int per = (int)((ntiles + want - 1) / want);
@@ -467,7 +588,7 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dt
   }
   p.ws_bytes = 0;
   if (p.nsplit > 1) {
-    const size_t rows = (size_t)B * Hkv * p.nqblk * kRowsPerBlock * p.nsplit;
+    const size_t rows = (size_t)B * Hkv * p.nqblk * p.rows * p.nsplit;
     p.ws_bytes = rows * D * sizeof(float) + rows * 2 * sizeof(float);
   }
   return p;
@@ -501,25 +622,20 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
   a.G = Hq / Hkv;
   a.Lcap = Lcap;
   a.max_seq_len = max_seq_len;
+  a.rows = plan.rows;
   a.nqblk = plan.nqblk;
   a.nsplit = plan.nsplit;
   a.chunk_len = plan.chunk_len;
   a.total_blocks = B * Hkv * plan.nqblk * plan.nsplit;
   a.anc_words = (N + 63) / 64;
-  a.anc_nodes = kRowsPerBlock / a.G + 2;
-  if (a.anc_nodes > N) a.anc_nodes = N;
   a.scale_log2 = scale * kLog2e;
   if (plan.nsplit > 1) {
-    const size_t rows = (size_t)B * Hkv * plan.nqblk * kRowsPerBlock * plan.nsplit;
+    const size_t rows = (size_t)B * Hkv * plan.nqblk * plan.rows * plan.nsplit;
     a.part_o = static_cast<float*>(ws);
     a.part_ml = static_cast<float*>(ws) + rows * D;
   }
-  const size_t lds = (size_t)a.anc_nodes * a.anc_words * sizeof(unsigned long long);
-  if (D == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(a.total_blocks), dim3(kThreads), lds, stream, a);
-  else
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(a.total_blocks), dim3(kThreads), lds, stream, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = (D == 128) ? launch_bf16<128>(a, plan.qbw, plan.nw, stream)
+                            : launch_bf16<64>(a, plan.qbw, plan.nw, stream);
   if (e != hipSuccess || plan.nsplit == 1) return e;
   const size_t items = (size_t)B * Hkv * N * a.G * (D / 4);
   const dim3 grid((unsigned)((items + 255) / 256));

@@ -73,7 +73,9 @@ __device__ __forceinline__ unsigned long long argmax_key(float f, uint32_t idx) 
 // ---------------------------------------------------------------- launchers
 
 struct AttnPlan {
-  int nqblk;      // query blocks of 128 rows per (sequence, KV head)
+  int qbw, nw;    // 16-row query blocks per wavefront, wavefronts per workgroup
+  int rows;       // query rows per workgroup (16 * qbw * nw)
+  int nqblk;      // query blocks per (sequence, KV head)
   int nsplit;     // workgroups along the prefix per query block
   int chunk_len;  // prefix keys per split (multiple of 64)
   size_t ws_bytes;
