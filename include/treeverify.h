@@ -111,9 +111,11 @@ int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
  * logits  [M][V] fp32 or NULL; written only when non-NULL (for checking:
  *         the step itself never materialises the logits)
  * workspace  at least tv_lmhead_argmax_workspace() bytes.  It must be
- *         zero-filled before its first use; every call leaves it zero-filled
- *         again when its kernel completes, so one buffer serves any number of
- *         calls in stream order (calls sharing it must not overlap).
+ *         zero-filled before its first use; every call leaves its first
+ *         8*M (rounded up to 256) + 256 bytes zero-filled again when it
+ *         completes (the rest, used when M > 64, is scratch), so one buffer
+ *         serves any number of calls in stream order, of any M up to the size
+ *         it was queried for (calls sharing it must not overlap).
  * Supported: bf16 needs K % 256 == 0; M >= 1, V >= 1.
  */
 size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype);

@@ -154,10 +154,32 @@ def test_lmhead_elementwise(name, packed):
     assert rel <= LOGITS_REL_L2, f"logits rel L2 {rel:.3e}"
     ref = oracle.lm_head_argmax(lm["hidden"], lm["w"], wl.dtype)
     assert_argmax_ok(arg.cpu().numpy(), ref, name)
-    # the workspace is left zeroed, and a second call (no logits) agrees
-    assert int(ws.count_nonzero()) == 0
+    # the zero region of the workspace is left zeroed, and a second call
+    # (no logits) agrees
+    zero_bytes = (M * 8 + 255) // 256 * 256 + 256
+    assert int(ws[:zero_bytes].count_nonzero()) == 0
     arg2 = tv.tv_lmhead_argmax(h, w, workspace=ws)
     np.testing.assert_array_equal(arg2.cpu().numpy(), arg.cpu().numpy())
+
+
+def test_lmhead_calls_of_different_m_share_one_workspace():
+    """Single-kernel (M <= 64) and partial-key (M > 64) calls in any order on
+    one workspace sized for the largest M."""
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = Q8.replace(B=1, N=300, hidden=512, V=3000, seed=39)
+    lm = lmhead_inputs(wl)
+    h_all = to_dev(lm["hidden"], "bf16")
+    w = to_dev(lm["w"], "bf16")
+    ref = oracle.lm_head_argmax(lm["hidden"], lm["w"], "bf16")
+    ws = torch.zeros(tv.tv_lmhead_argmax_workspace(300, 512, 3000), dtype=torch.uint8,
+                     device="cuda")
+    wp = tv.tv_lmhead_pack_weights(w)
+    for M in (300, 64, 100, 7, 300, 129):
+        for wt in (w, wp):
+            arg = tv.tv_lmhead_argmax(h_all[:M].contiguous(), wt, workspace=ws).cpu().numpy()
+            sub = {k: v[:M] for k, v in ref.items()}
+            assert_argmax_ok(arg, sub, f"M={M}")
 
 
 def test_pack_layout_matches_definition():

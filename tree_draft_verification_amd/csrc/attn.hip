@@ -46,7 +46,11 @@ namespace {
 
 constexpr int kKT = 64;     // keys per tile
 constexpr int kKPad = 8;    // bf16 padding of a K row in LDS
-constexpr int kVPad = 4;    // bf16 padding of a V^T row in LDS
+// V^T rows in LDS are unpadded; the 4-key (8-byte) units of row d are
+// XOR-swizzled by vt_swz(d), which makes both the transposing stores (16
+// lanes on 16 rows 8 apart) and the PV operand reads (16 lanes on 16
+// consecutive rows) free of bank conflicts.
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) ^ d) & 15; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.f;  // rescale when a score exceeds the reference by 2^8
 
@@ -102,7 +106,7 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int DS = D / 32;  // k-steps of the QK^T product
   constexpr int DB = D / 16;  // 16-row output blocks of the PV product
   constexpr int KROW = D + kKPad;
-  constexpr int VROW = kKT + kVPad;
+  constexpr int VROW = kKT;
   constexpr int KP_TOTAL = kKT * D / 8;           // 16-byte pieces of a K tile
   constexpr int KP = (KP_TOTAL + kThreads - 1) / kThreads;
   constexpr int VI_TOTAL = (kKT / 4) * (D / 8);   // 4-key x 8-dim items of a V tile
@@ -277,7 +281,8 @@ void attn_bf16_kernel(AttnArgs a) {
         uint2 pk;
         pk.x = ((w0[e >> 1] >> sh) & 0xffffu) | (((w1[e >> 1] >> sh) & 0xffffu) << 16);
         pk.y = ((w2[e >> 1] >> sh) & 0xffffu) | (((w3[e >> 1] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint2*>(&sVt[(x * 8 + e) * VROW + kq * 4]) = pk;
+        const int d = x * 8 + e;
+        *reinterpret_cast<uint2*>(&sVt[d * VROW + ((kq ^ vt_swz(d)) << 2)]) = pk;
       }
     }
   };
@@ -366,10 +371,11 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16_t* vrow = &sVt[(db * 16 + l16) * VROW + 32 * u + 4 * kg];
+        const int d = db * 16 + l16;
+        const bf16_t* vrow = &sVt[d * VROW];
         Frag8 vf;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((8 * u + kg) ^ vt_swz(d)) << 2));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((8 * u + kg + 4) ^ vt_swz(d)) << 2));
         vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) o[qb][db] = mfma16x16x32(vf.v, pf[qb][u].v, o[qb][db]);

@@ -6,77 +6,91 @@
 // uses its own offset (EQSPEC/EXSPEC abstract, arXiv 2510.22876 on the RSS
 // reader page: ragged acceptance must keep every sequence's KV state in step).
 //
-// In-place hazard: move j reads row L+path[j], which a parallel move j' < j
-// may be writing when path[j] == j'.  Each workgroup owns one (sequence,
-// head, K-or-V) plane, loads every moved row into LDS, waits at a barrier and
-// only then writes, so the result equals the serial order.  The loads and
-// stores are 16-byte vector accesses, consecutive threads on consecutive
-// 16-byte pieces of a row.
+// One workgroup per sequence handles every plane (K and V of every KV head)
+// and then updates that sequence's length itself, so one launch does the
+// whole commit.  In-place hazard: move j reads row L+path[j], which move
+// j' < j may be writing when path[j] == j'; the hazard exists only inside a
+// plane.  The workgroup therefore stages whole planes - all moved rows of a
+// group of planes - in LDS, waits at a barrier and only then writes.  Rows
+// with path[j] == j are skipped.  Accesses are 16-byte vectors, consecutive
+// threads on consecutive 16-byte pieces of a row.
 #include "tv_internal.h"
 
 namespace tv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
+constexpr int kStageBytes = 64 * 1024;  // LDS staging per workgroup
 
 __global__ __launch_bounds__(kThreads) void compact_kernel(
-    char* __restrict__ kc, char* __restrict__ vc, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ path, const int32_t* __restrict__ path_len, int Hkv,
-    int Lcap, int P, int row_bytes) {
-  extern __shared__ uint4 stage[];  // [P][row_bytes / 16]
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  char* plane = (blockIdx.z ? vc : kc) + ((size_t)b * Hkv + h) * (size_t)Lcap * row_bytes;
+    char* __restrict__ kc, char* __restrict__ vc, int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ path, const int32_t* __restrict__ path_len, int Hkv, int Lcap,
+    int P, int row_bytes) {
+  __shared__ uint4 stage[kStageBytes / 16];
+  __shared__ int16_t s_move[64];  // j of every row that moves
+  __shared__ int s_nmove;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
   const int L = seq_lens[b];
   int n = path_len[b];
   n = n < 0 ? 0 : (n > P ? P : n);
-  if (L < 0 || L + n > Lcap) return;  // caller contract broken: touch nothing
+  // caller contract broken: touch nothing (the length is left as it was)
+  if (L < 0 || L + n > Lcap) return;
   const int32_t* pth = path + (size_t)b * P;
-  const int chunks = row_bytes / 16;
-  const int total = n * chunks;
-
-  for (int c = threadIdx.x; c < total; c += kThreads) {
-    const int j = c / chunks;
-    const int x = c - j * chunks;
-    const int src = pth[j];
-    if (src != j && src >= 0 && L + src < Lcap)
-      stage[c] = reinterpret_cast<const uint4*>(plane + (size_t)(L + src) * row_bytes)[x];
+  if (tid == 0) {
+    int m = 0;
+    for (int j = 0; j < n; ++j) {
+      const int src = pth[j];
+      if (src != j && src >= 0 && L + src < Lcap) s_move[m++] = (int16_t)j;
+    }
+    s_nmove = m;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < total; c += kThreads) {
-    const int j = c / chunks;
-    const int x = c - j * chunks;
-    const int src = pth[j];
-    if (src != j && src >= 0 && L + src < Lcap)
-      reinterpret_cast<uint4*>(plane + (size_t)(L + j) * row_bytes)[x] = stage[c];
+  const int m = s_nmove;
+  const int chunks = row_bytes / 16;
+  const int per_plane = m * chunks;  // staged pieces per plane
+  const int planes = 2 * Hkv;
+  if (per_plane > 0) {
+    const int group = (kStageBytes / 16) / per_plane;  // >= 1: P * row_bytes <= 64 KB
+    for (int p0 = 0; p0 < planes; p0 += group) {
+      const int pn = min(group, planes - p0);
+      const int items = pn * per_plane;
+      for (int it = tid; it < items; it += kThreads) {
+        const int p = p0 + it / per_plane;
+        const int rem = it - (it / per_plane) * per_plane;
+        const int k = rem / chunks;
+        const int x = rem - k * chunks;
+        const char* plane = (p < Hkv ? kc : vc) +
+                            ((size_t)b * Hkv + (p < Hkv ? p : p - Hkv)) * (size_t)Lcap * row_bytes;
+        const int j = s_move[k];
+        stage[it] = reinterpret_cast<const uint4*>(plane + (size_t)(L + pth[j]) * row_bytes)[x];
+      }
+      __syncthreads();
+      for (int it = tid; it < items; it += kThreads) {
+        const int p = p0 + it / per_plane;
+        const int rem = it - (it / per_plane) * per_plane;
+        const int k = rem / chunks;
+        const int x = rem - k * chunks;
+        char* plane = (p < Hkv ? kc : vc) +
+                      ((size_t)b * Hkv + (p < Hkv ? p : p - Hkv)) * (size_t)Lcap * row_bytes;
+        const int j = s_move[k];
+        reinterpret_cast<uint4*>(plane + (size_t)(L + j) * row_bytes)[x] = stage[it];
+      }
+      __syncthreads();
+    }
   }
-}
-
-// Runs after every plane of the batch has read the old lengths.
-__global__ void seqlen_kernel(int32_t* __restrict__ seq_lens,
-                              const int32_t* __restrict__ path_len, int B, int P) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) {
-    int n = path_len[b];
-    n = n < 0 ? 0 : (n > P ? P : n);
-    seq_lens[b] += n;
-  }
+  if (tid == 0) seq_lens[b] = L + n;  // every thread read L before the barriers above
 }
 
 }  // namespace
 
 hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t* path,
-                             const int32_t* path_len, int B, int Hkv, int D, int Lcap,
-                             int P, int dtype, hipStream_t stream) {
+                             const int32_t* path_len, int B, int Hkv, int D, int Lcap, int P,
+                             int dtype, hipStream_t stream) {
   const int row_bytes = D * (dtype == TV_F32 ? 4 : 2);
-  const size_t lds = (size_t)P * row_bytes;
-  hipLaunchKernelGGL(compact_kernel, dim3(Hkv, B, 2), dim3(kThreads), lds, stream,
-                     static_cast<char*>(k), static_cast<char*>(v), seq_lens, path,
-                     path_len, Hkv, Lcap, P, row_bytes);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(seqlen_kernel, dim3((B + 255) / 256), dim3(256), 0, stream,
-                     seq_lens, path_len, B, P);
+  hipLaunchKernelGGL(compact_kernel, dim3(B), dim3(kThreads), 0, stream,
+                     static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len, Hkv,
+                     Lcap, P, row_bytes);
   return hipGetLastError();
 }
 

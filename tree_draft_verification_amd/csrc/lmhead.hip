@@ -38,7 +38,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVT = 128;        // vocabulary rows per workgroup (32 per wavefront)
-constexpr int kMT = 64;         // hidden-state rows per workgroup
 constexpr int kKC = 128;        // k per pipeline stage
 constexpr int kHRow = kKC + 8;  // LDS row of the hidden-state slice (bf16)
 
@@ -86,14 +85,17 @@ __device__ __forceinline__ size_t packed_offset(int vt, int c, int nk, int j, in
   return (((((size_t)vt * nk + c) * 8 + j) * 4 + s) * 64 + lane) * 8;
 }
 
-template <bool PACKED>
-__global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
-    const bf16_t* __restrict__ H, const bf16_t* __restrict__ W, int32_t* __restrict__ argmax,
-    float* __restrict__ logits, unsigned long long* __restrict__ keys,
-    unsigned* __restrict__ counter, int M, int K, int V, int nmt, int total_blocks) {
-  __shared__ __attribute__((aligned(16))) bf16_t sH[2][kMT * kHRow];
-  __shared__ unsigned long long s_wkey[4][kMT];
-  __shared__ unsigned long long s_rowkey[kMT];
+template <bool PACKED, int MB, bool PARTIAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MB == 4 ? 2 : 1)))
+void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
+                        int32_t* __restrict__ argmax, float* __restrict__ logits,
+                        unsigned long long* __restrict__ keys, unsigned* __restrict__ counter,
+                        int M, int K, int V, int nmt, int total_blocks) {
+  constexpr int kRowsM = 16 * MB;                  // hidden-state rows per workgroup
+  constexpr int HP = kRowsM * (kKC / 8) / kThreads;  // 16-byte H pieces per thread per stage
+  __shared__ __attribute__((aligned(16))) bf16_t sH[2][kRowsM * kHRow];
+  __shared__ unsigned long long s_wkey[4][kRowsM];
+  __shared__ unsigned long long s_rowkey[kRowsM];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
   const int lid = xcd_remap(blockIdx.x, total_blocks);
   const int mt = lid % nmt;
   const int vt = lid / nmt;
-  const int m0 = mt * kMT;
+  const int m0 = mt * kRowsM;
   const int v0 = vt * kVT;
   const int nk = K / kKC;
 
@@ -122,11 +124,11 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
     else
       return *reinterpret_cast<const uint4*>(wrow[vb] + c * kKC + 8 * s);
   };
-  // this thread's four 16-byte pieces of each hidden-state stage
-  const bf16_t* hsrc[4];
-  int hdst[4];
+  // this thread's 16-byte pieces of each hidden-state stage (clamped rows)
+  const bf16_t* hsrc[HP];
+  int hdst[HP];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < HP; ++i) {
     const int c = tid + i * kThreads;
     const int r = c >> 4;
     const int x = c & 15;
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
   }
 
   uint4 wb[2][2][4];  // [ring slot][16-row block][piece]
-  uint4 hreg[4];
+  uint4 hreg[HP];
 #pragma unroll
   for (int d = 0; d < 2; ++d)
 #pragma unroll
@@ -143,16 +145,16 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s) wb[d][vb][s] = wload(min(d, nk - 1), vb, s);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i]);
+  for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sH[0][hdst[i]]) = hreg[i];
+  for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(&sH[0][hdst[i]]) = hreg[i];
   __syncthreads();
 
-  f32x4_t acc[2][4];
+  f32x4_t acc[2][MB];
 #pragma unroll
   for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[vb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // nk is even (K is a multiple of 256): two chunks per trip keep the ring
   // slot and the LDS buffer compile-time constants.
@@ -162,20 +164,20 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
       const int c = c0 + u;
       const int ch = min(c + 1, nk - 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i] + ch * kKC);
+      for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i] + ch * kKC);
       const bf16_t* sh = sH[u];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        Frag8 hf[4];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          hf[mb].u = *reinterpret_cast<const uint4*>(&sh[(mb * 16 + l16) * kHRow + 32 * kg + 8 * s]);
+        for (int mb = 0; mb < MB; ++mb) {
+          Frag8 hf;
+          hf.u = *reinterpret_cast<const uint4*>(&sh[(mb * 16 + l16) * kHRow + 32 * kg + 8 * s]);
 #pragma unroll
-        for (int vb = 0; vb < 2; ++vb) {
-          Frag8 wf;
-          wf.u = wb[u][vb][s];
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) acc[vb][mb] = mfma16x16x32(wf.v, hf[mb].v, acc[vb][mb]);
+          for (int vb = 0; vb < 2; ++vb) {
+            Frag8 wf;
+            wf.u = wb[u][vb][s];
+            acc[vb][mb] = mfma16x16x32(wf.v, hf.v, acc[vb][mb]);
+          }
         }
       }
       const int cw = min(c + 2, nk - 1);
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) wb[u][vb][s] = wload(cw, vb, s);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sH[u ^ 1][hdst[i]]) = hreg[i];
+      for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(&sH[u ^ 1][hdst[i]]) = hreg[i];
       __syncthreads();
     }
   }
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
   // ---- epilogue: lane holds rows v = v0 + wave*32 + vb*16 + 4*kg + r of
   // hidden-state row m = m0 + mb*16 + l16
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + mb * 16 + l16;
     unsigned long long best = 0ull;
 #pragma unroll
@@ -224,14 +226,39 @@ __global__ __launch_bounds__(kThreads, 2) void lmhead_bf16_kernel(
     if (kg == 0) s_wkey[wave][mb * 16 + l16] = best;
   }
   __syncthreads();
-  if (tid < kMT) {
+  if (tid < kRowsM) {
     unsigned long long k = s_wkey[0][tid];
 #pragma unroll
     for (int w = 1; w < 4; ++w) k = s_wkey[w][tid] > k ? s_wkey[w][tid] : k;
     s_rowkey[tid] = k;
   }
   __syncthreads();
-  argmax_commit(keys, counter, argmax, M, total_blocks, m0, kMT, s_rowkey);
+  if constexpr (PARTIAL) {
+    // one key per (row, vocabulary tile); argmax_reduce_kernel finishes
+    const int nvt = total_blocks / nmt;
+    if (tid < kRowsM && m0 + tid < M) keys[(size_t)(m0 + tid) * nvt + vt] = s_rowkey[tid];
+  } else {
+    argmax_commit(keys, counter, argmax, M, total_blocks, m0, kRowsM, s_rowkey);
+  }
+}
+
+// Finish of the partial-key form: one wavefront per row takes the maximum
+// over the row's per-tile keys.
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const unsigned long long* __restrict__ part,
+                                                            int32_t* __restrict__ argmax, int M,
+                                                            int nvt) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (m >= M) return;
+  const unsigned long long* row = part + (size_t)m * nvt;
+  unsigned long long best = 0ull;
+  for (int i = lane; i < nvt; i += 64) best = row[i] > best ? row[i] : best;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const unsigned long long o = shfl_xor_u64(best, off);
+    best = o > best ? o : best;
+  }
+  if (lane == 0) argmax[m] = (int32_t)(~(uint32_t)(best & 0xffffffffull));
 }
 
 // Row-major [V][K] -> packed layout; one thread per 16-byte packed piece,
@@ -321,9 +348,21 @@ __global__ __launch_bounds__(kThreads) void lmhead_f32_kernel(
 
 }  // namespace
 
-size_t lmhead_ws_bytes(int M, int /*K*/, int /*V*/, int /*dtype*/) {
-  // per-row keys, then the completion counter on its own 256-byte line
-  return ((size_t)M * 8 + 255) / 256 * 256 + 256;
+// Hidden-state rows per workgroup of the bf16 kernel: up to 64 rows keep the
+// single-kernel argmax; larger M uses 128-row blocks (each vocabulary tile
+// then feeds twice the products) and finishes with argmax_reduce_kernel.
+// 256-row blocks measured slower: they fit only one workgroup per CU.
+static int lmhead_mb(int M) { return M <= 64 ? 4 : 8; }
+
+// Workspace: per-row keys, then the completion counter on its own 256-byte
+// line (this region is zero between calls), then - for the partial-key form
+// only - one key per (row, vocabulary tile), overwritten by every call.
+static size_t lmhead_zero_bytes(int M) { return ((size_t)M * 8 + 255) / 256 * 256 + 256; }
+
+size_t lmhead_ws_bytes(int M, int /*K*/, int V, int dtype) {
+  size_t bytes = lmhead_zero_bytes(M);
+  if (dtype == TV_BF16 && lmhead_mb(M) != 4) bytes += (size_t)M * ((V + kVT - 1) / kVT) * 8;
+  return bytes;
 }
 
 size_t lmhead_packed_bytes(int V, int K) {
@@ -352,17 +391,29 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
                        logits, keys, counter, M, K, V, nmt, total);
     return hipGetLastError();
   }
-  const int nmt = (M + kMT - 1) / kMT;
+  const int mb = lmhead_mb(M);
+  const int nmt = (M + 16 * mb - 1) / (16 * mb);
   const int nvt = (V + kVT - 1) / kVT;
   const int total = nmt * nvt;
   const bf16_t* h = static_cast<const bf16_t*>(hidden);
   const bf16_t* wv = static_cast<const bf16_t*>(w);
-  if (w_layout == TV_LAYOUT_PACKED)
-    hipLaunchKernelGGL(lmhead_bf16_kernel<true>, dim3(total), dim3(kThreads), 0, stream, h, wv,
-                       argmax, logits, keys, counter, M, K, V, nmt, total);
-  else
-    hipLaunchKernelGGL(lmhead_bf16_kernel<false>, dim3(total), dim3(kThreads), 0, stream, h, wv,
-                       argmax, logits, keys, counter, M, K, V, nmt, total);
+  const bool pk = w_layout == TV_LAYOUT_PACKED;
+  const dim3 grid(total), block(kThreads);
+  if (mb != 4)
+    keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lmhead_zero_bytes(M));
+#define TV_LM_LAUNCH(P, MBV, PART)                                                          \
+  hipLaunchKernelGGL((lmhead_bf16_kernel<P, MBV, PART>), grid, block, 0, stream, h, wv, argmax, \
+                     logits, keys, counter, M, K, V, nmt, total)
+  if (mb == 4) {
+    if (pk) TV_LM_LAUNCH(true, 4, false); else TV_LM_LAUNCH(false, 4, false);
+  } else {
+    if (pk) TV_LM_LAUNCH(true, 8, true); else TV_LM_LAUNCH(false, 8, true);
+  }
+#undef TV_LM_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || mb == 4) return e;
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, keys, argmax,
+                     M, nvt);
   return hipGetLastError();
 }
 
