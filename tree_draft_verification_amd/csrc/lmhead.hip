@@ -119,10 +119,16 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
     wrow[vb] = W + (size_t)(v < V ? v : V - 1) * K + 32 * kg;
   }
   auto wload = [&](int c, int vb, int s) -> uint4 {
-    if constexpr (PACKED)
-      return *reinterpret_cast<const uint4*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane));
-    else
+    if constexpr (PACKED) {
+      // streamed once: non-temporal (measured 6% faster on the packed layout,
+      // slower on the row-major one)
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 t = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane)));
+      return make_uint4(t.x, t.y, t.z, t.w);
+    } else {
       return *reinterpret_cast<const uint4*>(wrow[vb] + c * kKC + 8 * s);
+    }
   };
   // this thread's 16-byte pieces of each hidden-state stage (clamped rows)
   const bf16_t* hsrc[HP];
