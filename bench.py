@@ -10,6 +10,10 @@ LM head, whose per-launch time is taken with HIP events on the launch
 stream), and the fp64 oracle timed on this host's cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--paged PAGE_SIZE]
+
+--paged keeps the key/value caches in pages of a shared pool (placed by a
+seeded random permutation) and runs the paged attention and compaction calls.
 """
 from __future__ import annotations
 
@@ -124,6 +128,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="page size of a paged key/value cache (0: contiguous caches)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many bytes")
     args = ap.parse_args()
@@ -138,7 +144,8 @@ def main():
     import torch
 
     import tree_draft_verification_amd as tv
-    from workloads import WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs
+    from workloads import (WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs,
+                           paged_layout)
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -155,7 +162,14 @@ def main():
     def i32(x):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
 
-    q, kc, vc = to_dev(a["q"]), to_dev(a["k_cache"]), to_dev(a["v_cache"])
+    q = to_dev(a["q"])
+    ps = args.paged
+    if ps:
+        pg = paged_layout(a["k_cache"], a["v_cache"], ps, seed=wl.seed + ps)
+        kc, vc = to_dev(pg["k_pages"]), to_dev(pg["v_pages"])
+        block_table = i32(pg["block_table"])
+    else:
+        kc, vc = to_dev(a["k_cache"]), to_dev(a["v_cache"])
     hid, w = to_dev(lm["hidden"]), to_dev(lm["w"])
     # The vocabulary projection is a static weight: repack it once, outside
     # the timed region, into the layout the LM-head kernel streams fastest.
@@ -171,8 +185,9 @@ def main():
     plen = torch.empty(wl.B, dtype=torch.int32, device=dev)
     bonus = torch.empty(wl.B, dtype=torch.int32, device=dev)
     dt = tv.TV_BF16 if wl.dtype == "bf16" else tv.TV_F32
-    attn_ws = torch.zeros(max(256, tv.tv_tree_verify_attn_workspace(
-        wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, max_len, dt)), dtype=torch.uint8, device=dev)
+    need = (tv.tv_tree_verify_attn_paged_workspace(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, max_len, ps, dt)
+            if ps else tv.tv_tree_verify_attn_workspace(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, max_len, dt))
+    attn_ws = torch.zeros(max(256, need), dtype=torch.uint8, device=dev)
     lm_ws = torch.zeros(tv.tv_lmhead_argmax_workspace(wl.M, wl.hidden, wl.V, dt),
                         dtype=torch.uint8, device=dev)
 
@@ -190,8 +205,12 @@ def main():
         lens.copy_(lens0)   # compaction advanced the lengths; restore the batch
         if events:
             events[0].record()
-        tv.tv_tree_verify_attn(q, kc, vc, lens, parent, out, max_seq_len=max_len,
-                               scale=a["scale"], workspace=attn_ws)
+        if ps:
+            tv.tv_tree_verify_attn_paged(q, kc, vc, block_table, lens, parent, out,
+                                         max_seq_len=max_len, scale=a["scale"], workspace=attn_ws)
+        else:
+            tv.tv_tree_verify_attn(q, kc, vc, lens, parent, out, max_seq_len=max_len,
+                                   scale=a["scale"], workspace=attn_ws)
         if events:
             events[1].record()
         tv.tv_lmhead_argmax(hid, w_step, argmax, workspace=lm_ws)
@@ -200,7 +219,10 @@ def main():
         tv.tv_tree_accept(parent, draft, argmax, P, path=path, path_len=plen, bonus=bonus)
         if events:
             events[3].record()
-        tv.tv_kv_compact(kc, vc, lens, path, plen)
+        if ps:
+            tv.tv_kv_compact_paged(kc, vc, block_table, lens, path, plen)
+        else:
+            tv.tv_kv_compact(kc, vc, lens, path, plen)
         if events:
             events[4].record()
 
@@ -261,10 +283,11 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wl.dtype, "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "dtype": wl.dtype, "data": "synthetic (seeded generator, Qwen3-shaped layers, simulated drafter)",
         "config": {"workload": wl.name, "batch": wl.B, "nodes": wl.N,
                    "prefix": [int(x) for x in a["seq_lens"]], "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "head_dim": wl.D, "hidden": wl.hidden, "vocab": wl.V,
+                   "kv_layout": f"paged{ps}" if ps else "contiguous",
                    "parallelism": "none (1 GPU)"},
         "step_us": round(step_us, 2),
         "mean_path_len": float(plen_h.mean()),

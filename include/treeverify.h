@@ -56,6 +56,7 @@ extern "C" {
 #define TV_STATUS_BAD_PARENT 1 /* parent[0] != -1 or parent[i] not in [0, i) */
 #define TV_STATUS_BAD_LEN    2 /* L_b < 0, L_b > max_seq_len or L_b+N > Lcap */
 #define TV_STATUS_DEPTH      4 /* accepted path longer than P                */
+#define TV_STATUS_BAD_PAGE   8 /* a block-table entry outside [0, num_pages) */
 
 #define TV_MAX_NODES 1024 /* N limit of every call                           */
 
@@ -93,6 +94,32 @@ int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                         int Lcap, int max_seq_len, float scale, int dtype,
                         void* workspace, size_t ws_bytes, int32_t* dev_status,
                         void* stream);
+
+/*
+ * Tree-causal attention over paged key/value caches (the engine of the
+ * JetSpec GitHub README, "Quick Start", keeps its KV cache in pages).
+ * Same computation as tv_tree_verify_attn; only where rows live differs:
+ *
+ * k_pages, v_pages  [num_pages][Hkv][page_size][D] bf16 pools (read only)
+ * block_table       [B][max_blocks] int32: logical row r of sequence b is
+ *                   row r % page_size of page block_table[b][r / page_size]
+ *                   (prefix rows 0..L-1, then the N tree rows L..L+N-1)
+ * page_size         power of two, 16..4096; max_seq_len + N must fit in
+ *                   max_blocks * page_size
+ * workspace         at least tv_tree_verify_attn_paged_workspace() bytes
+ * Device-side checks add TV_STATUS_BAD_PAGE (an entry outside the pool;
+ * it is never dereferenced).  bf16 only (TV_ENOTSUP otherwise).
+ */
+size_t tv_tree_verify_attn_paged_workspace(int B, int N, int Hq, int Hkv, int D,
+                                           int max_seq_len, int page_size, int dtype);
+int tv_tree_verify_attn_paged(const void* q, const void* k_pages,
+                              const void* v_pages, const int32_t* block_table,
+                              int max_blocks, int page_size, int num_pages,
+                              const int32_t* seq_lens, const int32_t* parent,
+                              void* out, int B, int N, int Hq, int Hkv, int D,
+                              int max_seq_len, float scale, int dtype,
+                              void* workspace, size_t ws_bytes,
+                              int32_t* dev_status, void* stream);
 
 /*
  * Target LM head fused with a per-row argmax (the accepted path follows the
@@ -179,6 +206,22 @@ int tv_tree_accept(const int32_t* parent, const int32_t* draft_tokens,
 int tv_kv_compact(void* k_cache, void* v_cache, int32_t* seq_lens,
                   const int32_t* path, const int32_t* path_len, int B, int Hkv,
                   int D, int Lcap, int P, int dtype, void* stream);
+
+/*
+ * KV compaction on paged caches (layout as for tv_tree_verify_attn_paged):
+ * the same row moves as tv_kv_compact, through the block table; a move
+ * whose page entry is outside the pool is skipped.  bf16 or fp32 pools,
+ * updated in place, with seq_lens[b] += path_len[b].  The caller guarantees
+ * L_b + path_len[b] <= max_blocks * page_size (else sequence b is left
+ * untouched) and that the pages holding rows L_b .. L_b+P-1 of a sequence
+ * belong to that sequence alone (pages of a shared prefix may be shared;
+ * tree rows may not).
+ */
+int tv_kv_compact_paged(void* k_pages, void* v_pages, const int32_t* block_table,
+                        int max_blocks, int page_size, int num_pages,
+                        int32_t* seq_lens, const int32_t* path,
+                        const int32_t* path_len, int B, int Hkv, int D, int P,
+                        int dtype, void* stream);
 
 /* Text of a status code (TV_EHIP: the HIP error text of the failed launch). */
 const char* tv_status_string(int status);

@@ -20,9 +20,12 @@ from .verify import (  # noqa: F401
     ancestors,
     decode,
     kv_compact,
+    kv_compact_paged,
     lm_head_argmax,
+    paged_to_contiguous,
     lm_logits,
     tree_accept,
     tree_attention,
+    tree_attention_paged,
     verify_step,
 )

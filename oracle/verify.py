@@ -230,6 +230,55 @@ def kv_compact(k_cache, v_cache, seq_lens, path, path_len):
 
 
 # ----------------------------------------------------------------------------
+# paged caches
+
+def paged_to_contiguous(pages, block_table, page_size, rows):
+    """Logical rows 0..rows-1 of every sequence, gathered from a page pool.
+
+    pages [num_pages][Hkv][page_size][D]; logical row r of sequence b lives
+    at pages[block_table[b][r // page_size], :, r % page_size].
+    """
+    pages = np.asarray(pages)
+    bt = np.asarray(block_table)
+    B = bt.shape[0]
+    Hkv, D = pages.shape[1], pages.shape[3]
+    out = np.empty((B, Hkv, rows, D), dtype=pages.dtype)
+    for b in range(B):
+        for r in range(rows):
+            out[b, :, r, :] = pages[bt[b, r // page_size], :, r % page_size, :]
+    return out
+
+
+def tree_attention_paged(q, k_pages, v_pages, block_table, page_size, seq_lens, parent,
+                         scale, dtype, nodes=None) -> np.ndarray:
+    """tree_attention on the logical rows that a block table names."""
+    rows = int(np.max(seq_lens)) + np.asarray(parent).shape[1]
+    k = paged_to_contiguous(k_pages, block_table, page_size, rows)
+    v = paged_to_contiguous(v_pages, block_table, page_size, rows)
+    return tree_attention(q, k, v, seq_lens, parent, scale, dtype, nodes=nodes)
+
+
+def kv_compact_paged(k_pages, v_pages, block_table, page_size, seq_lens, path, path_len):
+    """kv_compact on paged caches: the same serial row moves, each row found
+    through the block table (copies; inputs untouched)."""
+    k = np.array(k_pages, copy=True)
+    v = np.array(v_pages, copy=True)
+    bt = np.asarray(block_table)
+    lens = np.array(seq_lens, dtype=np.int32, copy=True)
+    for b in range(bt.shape[0]):
+        L = int(lens[b])
+        n = int(path_len[b])
+        for j in range(n):
+            s = int(path[b, j])
+            if s != j:
+                ps, pd = bt[b, (L + s) // page_size], bt[b, (L + j) // page_size]
+                k[pd, :, (L + j) % page_size, :] = k[ps, :, (L + s) % page_size, :]
+                v[pd, :, (L + j) % page_size, :] = v[ps, :, (L + s) % page_size, :]
+        lens[b] = L + n
+    return k, v, lens
+
+
+# ----------------------------------------------------------------------------
 # the whole step
 
 def verify_step(att: dict, lm: dict, draft, dtype: str, P: int = 32,

@@ -40,7 +40,8 @@ def test_header_declares_the_four_calls():
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
-              "tv_status_string", "tv_abi_version"):
+              "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
+              "tv_kv_compact_paged", "tv_status_string", "tv_abi_version"):
         assert n in names
 
 
@@ -134,11 +135,51 @@ def test_accept_and_compact_host_validation(lib):
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 2048, 32, 3, None) == -2
 
 
+def _attn_paged(lib, **kw):
+    a = dict(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, mb=68, ps=16, npg=100, sl=FAKE, par=FAKE,
+             out=FAKE, B=1, N=64, Hq=32, Hkv=8, D=128, msl=1024, scale=0.088, dtype=0, ws=FAKE,
+             wsb=1 << 30, st=None, stream=None)
+    a.update(kw)
+    return lib.tv_tree_verify_attn_paged(
+        a["q"], a["kp"], a["vp"], a["bt"], a["mb"], a["ps"], a["npg"], a["sl"], a["par"],
+        a["out"], a["B"], a["N"], a["Hq"], a["Hkv"], a["D"], a["msl"], a["scale"], a["dtype"],
+        a["ws"], a["wsb"], a["st"], a["stream"])
+
+
+def test_paged_host_validation(lib):
+    assert _attn_paged(lib, bt=None) == -1
+    assert _attn_paged(lib, ps=24) == -1                 # not a power of two
+    assert _attn_paged(lib, ps=8) == -1                  # below 16 rows
+    assert _attn_paged(lib, mb=67) == -1                 # 67 * 16 < 1024 + 64
+    assert _attn_paged(lib, npg=0) == -1
+    assert _attn_paged(lib, Hq=30) == -1
+    assert _attn_paged(lib, dtype=1) == -2               # paged attention: bf16 only
+    assert _attn_paged(lib, D=96) == -2
+    assert _attn_paged(lib, N=1025, mb=200) == -2
+    need = lib.tv_tree_verify_attn_paged_workspace(1, 64, 32, 8, 128, 1024, 16, 0)
+    assert need > 0
+    assert _attn_paged(lib, ws=None) == -3
+    assert _attn_paged(lib, wsb=need - 1) == -3
+    assert lib.tv_tree_verify_attn_paged_workspace(1, 64, 32, 8, 128, 1024, 12, 0) == 0
+    # a long prefix with small pages is split so that one split's page
+    # entries fit the workgroup's cache: more splits than the contiguous plan
+    long_c = lib.tv_tree_verify_attn_workspace(1, 64, 32, 8, 128, 1 << 20, 0)
+    long_p = lib.tv_tree_verify_attn_paged_workspace(1, 64, 32, 8, 128, 1 << 20, 16, 0)
+    assert long_p > long_c > 0
+    c = lib.tv_kv_compact_paged
+    assert c(None, FAKE, FAKE, 68, 16, 100, FAKE, FAKE, FAKE, 1, 8, 128, 32, 0, None) == -1
+    assert c(FAKE, FAKE, FAKE, 68, 20, 100, FAKE, FAKE, FAKE, 1, 8, 128, 32, 0, None) == -1
+    assert c(FAKE, FAKE, FAKE, 0, 16, 100, FAKE, FAKE, FAKE, 1, 8, 128, 32, 0, None) == -1
+    assert c(FAKE, FAKE, FAKE, 68, 16, 100, FAKE, FAKE, FAKE, 1, 8, 4, 32, 0, None) == -2
+    assert c(FAKE, FAKE, FAKE, 68, 16, 100, FAKE, FAKE, FAKE, 1, 8, 128, 65, 0, None) == -2
+
+
 def test_binding_names_match_the_c_calls():
     import tree_draft_verification_amd as tv
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
-              "tv_status_string", "tv_abi_version"):
+              "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
+              "tv_kv_compact_paged", "tv_status_string", "tv_abi_version"):
         assert callable(getattr(tv, n))
     assert tv.tv_status_string(-3) == "workspace missing or too small"

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs
+from workloads import (WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs,
+                       paged_layout)
 
 from _helpers import (LOGITS_REL_L2, assert_argmax_ok, assert_attn_close, i32_dev, to_dev,
                       to_host_bits, to_host_f64)
@@ -115,3 +116,45 @@ def test_full_size_step(name):
     np.testing.assert_array_equal(gk, k2)
     np.testing.assert_array_equal(gv, v2)
     print(f"[full] {name}: path_len={acc['path_len'].tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("name,ps", [("qwen3_8b_L1024_N64", 64), ("qwen3_8b_L16384_N256", 16),
+                                     ("qwen3_8b_ragged8_N64", 16),
+                                     ("qwen3_30b_a3b_B4_L4096_N1024", 64)])
+def test_full_size_paged(name, ps):
+    """Attention and compaction through a block table at full size: pages
+    of a shared pool placed by a random permutation."""
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = WORKLOADS[name]
+    a = attn_inputs(wl)
+    pg = paged_layout(a["k_cache"], a["v_cache"], ps, seed=wl.seed + ps)
+    print(f"[full-paged] {name}: ps={ps} pages={pg['num_pages']} L={list(a['seq_lens'])}",
+          flush=True)
+    kp, vp = to_dev(pg["k_pages"], wl.dtype), to_dev(pg["v_pages"], wl.dtype)
+    bt, lens, par = i32_dev(pg["block_table"]), i32_dev(a["seq_lens"]), i32_dev(a["parent"])
+    st = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+    out = tv.tv_tree_verify_attn_paged(to_dev(a["q"], wl.dtype), kp, vp, bt, lens, par,
+                                       max_seq_len=int(a["seq_lens"].max()), scale=a["scale"],
+                                       dev_status=st)
+    rng = np.random.default_rng(wl.seed + 3)
+    tgt = rng.integers(0, 50, size=(wl.B, wl.N)).astype(np.int32)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt)
+    acc = oracle.tree_accept(a["parent"], draft, tgt, 32)
+    tv.tv_kv_compact_paged(kp, vp, bt, lens, i32_dev(acc["path"]), i32_dev(acc["path_len"]))
+    torch.cuda.synchronize()
+    assert st.cpu().numpy().tolist() == [0] * wl.B
+
+    nodes = _sample(wl.N, ATTN_SAMPLE[name], wl.seed)
+    ref_o = oracle.tree_attention_paged(a["q"], pg["k_pages"], pg["v_pages"], pg["block_table"],
+                                        ps, a["seq_lens"], a["parent"], a["scale"], wl.dtype,
+                                        nodes=nodes)
+    mx, rel = assert_attn_close(to_host_f64(out), ref_o, name)
+    print(f"[full-paged] {name}: attention max|d|={mx:.2e} rel={rel:.2e}", flush=True)
+
+    k2, v2, lens2 = oracle.kv_compact_paged(pg["k_pages"], pg["v_pages"], pg["block_table"], ps,
+                                            a["seq_lens"], acc["path"], acc["path_len"])
+    np.testing.assert_array_equal(lens.cpu().numpy(), lens2)
+    np.testing.assert_array_equal(to_host_bits(kp), k2)
+    np.testing.assert_array_equal(to_host_bits(vp), v2)
+    print(f"[full-paged] {name}: path_len={acc['path_len'].tolist()}", flush=True)

@@ -7,7 +7,8 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs
+from workloads import (WORKLOADS, attn_inputs, draft_coins, draft_tokens, lmhead_inputs,
+                       paged_layout)
 
 from _helpers import (LOGITS_REL_L2, assert_argmax_ok, assert_attn_close, i32_dev,
                       to_dev, to_host_bits, to_host_f64)
@@ -379,3 +380,119 @@ def test_step_end_to_end_small(name):
     if wl.dtype == "f32":
         gk, k2 = gk.view(np.uint32), k2.view(np.uint32)
     np.testing.assert_array_equal(gk, k2)
+
+
+# ---------------------------------------------------------------- paged caches
+
+PAGED_CASES = {
+    "q8_ragged3_N64_ps16": ("q8_ragged3_N64", 16),
+    "a3b_B2_L257_N200_ps64": ("a3b_B2_L257_N200", 64),
+    "q8_bfs_L1000_N256_ps256": ("q8_bfs_L1000_N256", 256),
+    "d64_bf16_L129_N33_ps32": ("d64_bf16_L129_N33", 32),
+    "empty_prefix_N20_ps16": ("empty_prefix_N20", 16),
+    "g1_L64_N130_ps128": ("g1_L64_N130", 128),
+}
+
+
+def _paged_dev(pg, dtype):
+    return (to_dev(pg["k_pages"], dtype), to_dev(pg["v_pages"], dtype),
+            i32_dev(pg["block_table"]))
+
+
+@pytest.mark.parametrize("name", list(PAGED_CASES))
+def test_attention_paged_elementwise(name):
+    """Paged attention == the oracle on the gathered rows; with no plan change
+    it also reproduces the contiguous kernel's bits."""
+    import torch
+    import tree_draft_verification_amd as tv
+    case, ps = PAGED_CASES[name]
+    wl = ATTN_CASES[case]
+    a = attn_inputs(wl)
+    pg = paged_layout(a["k_cache"], a["v_cache"], ps, seed=wl.seed + ps)
+    print(f"[attn-paged] {name} B={wl.B} N={wl.N} L={list(a['seq_lens'])} "
+          f"pages={pg['num_pages']}", flush=True)
+    kp, vp, bt = _paged_dev(pg, wl.dtype)
+    st = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+    msl = int(a["seq_lens"].max())
+    out = tv.tv_tree_verify_attn_paged(to_dev(a["q"], wl.dtype), kp, vp, bt,
+                                       i32_dev(a["seq_lens"]), i32_dev(a["parent"]),
+                                       max_seq_len=msl, scale=a["scale"], dev_status=st)
+    assert st.cpu().tolist() == [0] * wl.B
+    ref = oracle.tree_attention_paged(a["q"], pg["k_pages"], pg["v_pages"], pg["block_table"],
+                                      ps, a["seq_lens"], a["parent"], a["scale"], wl.dtype)
+    assert_attn_close(to_host_f64(out), ref, name)
+    if (tv.tv_tree_verify_attn_paged_workspace(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, msl, ps)
+            == tv.tv_tree_verify_attn_workspace(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D, msl)):
+        np.testing.assert_array_equal(to_host_bits(out), to_host_bits(_run_attn(a, wl)))
+
+
+def test_attention_paged_flags_bad_page():
+    """A block-table entry outside the pool flags its sequence only."""
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = ATTN_CASES["q8_ragged3_N64"]
+    a = attn_inputs(wl)
+    pg = paged_layout(a["k_cache"], a["v_cache"], 16, seed=5)
+    bt = pg["block_table"].copy()
+    bt[1, 0] = pg["num_pages"]               # first prefix block of sequence 1
+    bt[2, int(a["seq_lens"][2]) // 16] = -7   # first tree block of sequence 2
+    kp, vp, _ = _paged_dev(pg, "bf16")
+    st = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+    out = tv.tv_tree_verify_attn_paged(to_dev(a["q"], "bf16"), kp, vp, i32_dev(bt),
+                                       i32_dev(a["seq_lens"]), i32_dev(a["parent"]),
+                                       max_seq_len=int(a["seq_lens"].max()), scale=a["scale"],
+                                       dev_status=st)
+    assert st.cpu().tolist() == [0, tv.TV_STATUS_BAD_PAGE, tv.TV_STATUS_BAD_PAGE]
+    ref = oracle.tree_attention(a["q"][:1], a["k_cache"][:1], a["v_cache"][:1],
+                                a["seq_lens"][:1], a["parent"][:1], a["scale"], "bf16")
+    assert_attn_close(to_host_f64(out)[:1], ref, "bad-page seq 0")
+
+
+@pytest.mark.parametrize("name,ps", [("tiny_fp32", 16), ("qwen3_8b_ragged8_N64", 16),
+                                     ("qwen3_30b_a3b_B4_L4096_N1024", 64)])
+def test_compact_paged_bit_exact(name, ps):
+    import tree_draft_verification_amd as tv
+    wl = WORKLOADS[name]
+    if name != "tiny_fp32":
+        wl = wl.replace(L_lo=min(wl.L_lo, 300), L_hi=min(wl.L_hi, 900))
+    a = attn_inputs(wl)
+    pg = paged_layout(a["k_cache"], a["v_cache"], ps, seed=wl.seed + 7)
+    rng = np.random.default_rng(45)
+    tgt = rng.integers(0, 20, size=(wl.B, wl.N)).astype(np.int32)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt)
+    acc = oracle.tree_accept(a["parent"], draft, tgt, P=32)
+    k2, v2, lens2 = oracle.kv_compact_paged(pg["k_pages"], pg["v_pages"], pg["block_table"], ps,
+                                            a["seq_lens"], acc["path"], acc["path_len"])
+    kp, vp, bt = _paged_dev(pg, wl.dtype)
+    lens = i32_dev(a["seq_lens"])
+    tv.tv_kv_compact_paged(kp, vp, bt, lens, i32_dev(acc["path"]), i32_dev(acc["path_len"]))
+    np.testing.assert_array_equal(lens.cpu().numpy(), lens2)
+    gk, gv = to_host_bits(kp), to_host_bits(vp)
+    if wl.dtype == "f32":
+        gk, gv, k2, v2 = (x.view(np.uint32) for x in (gk, gv, k2, v2))
+    np.testing.assert_array_equal(gk, k2)
+    np.testing.assert_array_equal(gv, v2)
+
+
+def test_compact_paged_hazard_rows_cross_pages():
+    """Moves whose source and destination rows sit on different pages, with
+    every row of the path moving (page size 16, path of stride 2)."""
+    import tree_draft_verification_amd as tv
+    B, Hkv, D, L, N, P, ps = 2, 3, 128, 13, 64, 32, 16
+    rng = np.random.default_rng(46)
+    kc = rng.integers(0, 65535, size=(B, Hkv, 96, D)).astype(np.uint16)
+    vc = rng.integers(0, 65535, size=(B, Hkv, 96, D)).astype(np.uint16)
+    pg = paged_layout(kc, vc, ps, seed=47)
+    path = np.full((B, P), -1, np.int32)
+    path[0, :20] = np.arange(0, 40, 2)
+    path[1, :32] = np.concatenate([[0], np.arange(1, 32) + 30])
+    plen = np.array([20, 32], np.int32)
+    lens = np.array([L, L + 1], np.int32)
+    k2, v2, lens2 = oracle.kv_compact_paged(pg["k_pages"], pg["v_pages"], pg["block_table"], ps,
+                                            lens, path, plen)
+    kp, vp, bt = _paged_dev(pg, "bf16")
+    sl = i32_dev(lens)
+    tv.tv_kv_compact_paged(kp, vp, bt, sl, i32_dev(path), i32_dev(plen))
+    np.testing.assert_array_equal(to_host_bits(kp), k2)
+    np.testing.assert_array_equal(to_host_bits(vp), v2)
+    np.testing.assert_array_equal(sl.cpu().numpy(), lens2)

@@ -430,3 +430,42 @@ def test_p10_cross_step_invariant():
                 V = v2[b, h // G, :Lb + j + 1].astype(np.float64)
                 w = _softmax_rows(0.4 * (K @ q[b, node, h].astype(np.float64))[None])[0]
                 np.testing.assert_allclose(w @ V, tree_out[b, node, h], atol=1e-12)
+
+
+# ---------------------------------------------------------------- paged caches
+
+
+def test_paged_oracle_matches_contiguous_under_any_page_placement():
+    """Pages placed by a random permutation hold the same logical rows: paged
+    attention and paged compaction equal the (pinned) contiguous results."""
+    from workloads import WORKLOADS, attn_inputs, paged_layout
+    wl = WORKLOADS["qwen3_8b_ragged8_N64"].replace(B=3, L_lo=40, L_hi=150, N=20, Hq=4, Hkv=2,
+                                                   D=16, seed=71)
+    a = attn_inputs(wl)
+    for ps in (16, 64):
+        pg = paged_layout(a["k_cache"], a["v_cache"], ps, seed=ps)
+        np.testing.assert_array_equal(
+            oracle.paged_to_contiguous(pg["k_pages"], pg["block_table"], ps, a["Lcap"]),
+            a["k_cache"])
+        got = oracle.tree_attention_paged(a["q"], pg["k_pages"], pg["v_pages"],
+                                          pg["block_table"], ps, a["seq_lens"], a["parent"],
+                                          a["scale"], "bf16")
+        ref = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"],
+                                    a["parent"], a["scale"], "bf16")
+        np.testing.assert_array_equal(got, ref)
+        rng = np.random.default_rng(ps)
+        P = 16
+        path = np.full((wl.B, P), -1, np.int32)
+        plen = np.zeros(wl.B, np.int32)
+        for b in range(wl.B):
+            walk = oracle.ancestors(a["parent"][b], int(rng.integers(0, wl.N)))[::-1]
+            path[b, :len(walk)] = walk
+            plen[b] = len(walk)
+        k2, v2, l2 = oracle.kv_compact_paged(pg["k_pages"], pg["v_pages"], pg["block_table"], ps,
+                                             a["seq_lens"], path, plen)
+        kc, vc, lc = oracle.kv_compact(a["k_cache"], a["v_cache"], a["seq_lens"], path, plen)
+        np.testing.assert_array_equal(l2, lc)
+        np.testing.assert_array_equal(
+            oracle.paged_to_contiguous(k2, pg["block_table"], ps, a["Lcap"]), kc)
+        np.testing.assert_array_equal(
+            oracle.paged_to_contiguous(v2, pg["block_table"], ps, a["Lcap"]), vc)

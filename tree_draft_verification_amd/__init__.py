@@ -22,7 +22,8 @@ import torch
 
 from . import _lib
 from ._lib import (TV_BF16, TV_F32, TV_LAYOUT_PACKED, TV_LAYOUT_ROWMAJOR,  # noqa: F401
-                   TV_MAX_NODES, TV_STATUS_BAD_LEN, TV_STATUS_BAD_PARENT, TV_STATUS_DEPTH)
+                   TV_MAX_NODES, TV_STATUS_BAD_LEN, TV_STATUS_BAD_PAGE, TV_STATUS_BAD_PARENT,
+                   TV_STATUS_DEPTH)
 
 _LIB_HANDLE = None
 
@@ -148,6 +149,47 @@ def tv_tree_verify_attn(q, k_cache, v_cache, seq_lens, parent, out=None, *,
     return out
 
 
+def tv_tree_verify_attn_paged_workspace(B, N, Hq, Hkv, D, max_seq_len, page_size,
+                                        dtype=TV_BF16) -> int:
+    return int(_lib_handle().tv_tree_verify_attn_paged_workspace(B, N, Hq, Hkv, D, max_seq_len,
+                                                                  page_size, dtype))
+
+
+def tv_tree_verify_attn_paged(q, k_pages, v_pages, block_table, seq_lens, parent, out=None, *,
+                              max_seq_len: int, scale: float | None = None,
+                              workspace: torch.Tensor | None = None,
+                              dev_status: torch.Tensor | None = None) -> torch.Tensor:
+    """Tree-causal attention over paged caches.  q [B,N,Hq,D];
+    pools [num_pages,Hkv,page_size,D]; block_table [B,max_blocks] int32."""
+    B, N, Hq, D = q.shape
+    num_pages, Hkv, page_size, Dk = k_pages.shape
+    if Dk != D or v_pages.shape != k_pages.shape:
+        raise ValueError("q and the page pools disagree")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise TypeError("q and the page pools must share a dtype")
+    Bt, max_blocks = block_table.shape
+    _i32(block_table, (B, max_blocks), "block_table")
+    _i32(seq_lens, (B,), "seq_lens")
+    _i32(parent, (B, N), "parent")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = tv_tree_verify_attn_paged_workspace(B, N, Hq, Hkv, D, max_seq_len, page_size, dt)
+    if workspace is None and need > 0:
+        workspace = _cached_workspace("attn", need, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib_handle().tv_tree_verify_attn_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), max_blocks, page_size,
+        num_pages, _ptr(seq_lens), _ptr(parent), _ptr(out), B, N, Hq, Hkv, D, int(max_seq_len),
+        float(scale), dt, _ptr(workspace), ws_bytes, _ptr(dev_status), _stream(q.device))
+    _check("tv_tree_verify_attn_paged", st)
+    return out
+
+
 # ---------------------------------------------------------------- LM head
 
 class PackedWeights:
@@ -257,3 +299,21 @@ def tv_kv_compact(k_cache, v_cache, seq_lens, path, path_len) -> None:
     st = _lib_handle().tv_kv_compact(_ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(path),
                             _ptr(path_len), B, Hkv, D, Lcap, P, dt, _stream(k_cache.device))
     _check("tv_kv_compact", st)
+
+
+def tv_kv_compact_paged(k_pages, v_pages, block_table, seq_lens, path, path_len) -> None:
+    """Paged compaction: the moves of tv_kv_compact through the block table."""
+    num_pages, Hkv, page_size, D = k_pages.shape
+    if v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages and v_pages disagree")
+    dt = _dtype_code(k_pages)
+    B, max_blocks = block_table.shape
+    _i32(block_table, (B, max_blocks), "block_table")
+    _i32(seq_lens, (B,), "seq_lens")
+    P = path.shape[1]
+    _i32(path, (B, P), "path")
+    _i32(path_len, (B,), "path_len")
+    st = _lib_handle().tv_kv_compact_paged(
+        _ptr(k_pages), _ptr(v_pages), _ptr(block_table), max_blocks, page_size, num_pages,
+        _ptr(seq_lens), _ptr(path), _ptr(path_len), B, Hkv, D, P, dt, _stream(k_pages.device))
+    _check("tv_kv_compact_paged", st)

@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libt
 TV_OK, TV_EINVAL, TV_ENOTSUP, TV_EWORKSPACE, TV_EHIP = 0, -1, -2, -3, -4
 TV_BF16, TV_F32 = 0, 1
 TV_LAYOUT_ROWMAJOR, TV_LAYOUT_PACKED = 0, 1
-TV_STATUS_BAD_PARENT, TV_STATUS_BAD_LEN, TV_STATUS_DEPTH = 1, 2, 4
+TV_STATUS_BAD_PARENT, TV_STATUS_BAD_LEN, TV_STATUS_DEPTH, TV_STATUS_BAD_PAGE = 1, 2, 4, 8
 TV_MAX_NODES = 1024
 
 _p = ctypes.c_void_p
@@ -21,6 +21,10 @@ SIGNATURES = {
     "tv_tree_verify_attn_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "tv_tree_verify_attn": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                                  _p, _sz, _p, _p]),
+    "tv_tree_verify_attn_paged_workspace": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "tv_tree_verify_attn_paged": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i,
+                                       _i, _i, _f, _i, _p, _sz, _p, _p]),
+    "tv_kv_compact_paged": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "tv_lmhead_argmax_workspace": (_sz, [_i, _i, _i, _i]),
     "tv_lmhead_argmax": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
     "tv_lmhead_packed_bytes": (_sz, [_i, _i, _i]),

@@ -39,7 +39,7 @@ const char* tv_status_string(int status) {
 size_t tv_tree_verify_attn_workspace(int B, int N, int Hq, int Hkv, int D, int max_seq_len,
                                      int dtype) {
   if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_seq_len < 0) return 0;
-  return tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype).ws_bytes;
+  return tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype, 0).ws_bytes;
 }
 
 int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -58,13 +58,68 @@ int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
   if (N > TV_MAX_NODES) return TV_ENOTSUP;
   if (dtype == TV_F32 && ((long long)N * Hq > 2147483647LL || B > 65535 || Hq > 65535))
     return TV_ENOTSUP;
-  const tv::AttnPlan plan = tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype);
+  const tv::AttnPlan plan = tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype, 0);
   if ((long long)B * Hkv * plan.nqblk * plan.nsplit > 2147483647LL) return TV_ENOTSUP;
   if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes)) return TV_EWORKSPACE;
   return hip_status(tv::launch_tree_attn(q, k_cache, v_cache, seq_lens, parent, out, B, N, Hq,
                                          Hkv, D, Lcap, max_seq_len, scale, dtype, plan,
                                          workspace, dev_status,
                                          static_cast<hipStream_t>(stream)));
+}
+
+static bool page_size_ok(int ps) { return ps >= 16 && ps <= 4096 && (ps & (ps - 1)) == 0; }
+
+size_t tv_tree_verify_attn_paged_workspace(int B, int N, int Hq, int Hkv, int D,
+                                           int max_seq_len, int page_size, int dtype) {
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || max_seq_len < 0 ||
+      !page_size_ok(page_size))
+    return 0;
+  return tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype, page_size).ws_bytes;
+}
+
+int tv_tree_verify_attn_paged(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, int max_blocks, int page_size,
+                              int num_pages, const int32_t* seq_lens, const int32_t* parent,
+                              void* out, int B, int N, int Hq, int Hkv, int D, int max_seq_len,
+                              float scale, int dtype, void* workspace, size_t ws_bytes,
+                              int32_t* dev_status, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !parent || !out)
+    return TV_EINVAL;
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || D < 1 || max_blocks < 1 || num_pages < 1 ||
+      max_seq_len < 0)
+    return TV_EINVAL;
+  if (Hq % Hkv) return TV_EINVAL;
+  if (!page_size_ok(page_size)) return TV_EINVAL;
+  if ((long long)max_seq_len + N > (long long)max_blocks * page_size) return TV_EINVAL;
+  if ((long long)max_blocks * page_size > 2147483647LL) return TV_EINVAL;
+  if (!isfinite(scale)) return TV_EINVAL;
+  if (dtype != TV_BF16) return TV_ENOTSUP;  // paged caches: bf16 kernel only
+  if (D != 64 && D != 128) return TV_ENOTSUP;
+  if (N > TV_MAX_NODES) return TV_ENOTSUP;
+  const tv::AttnPlan plan = tv::attn_plan(B, N, Hq, Hkv, D, max_seq_len, dtype, page_size);
+  if ((long long)B * Hkv * plan.nqblk * plan.nsplit > 2147483647LL) return TV_ENOTSUP;
+  if (plan.ws_bytes > 0 && (!workspace || ws_bytes < plan.ws_bytes)) return TV_EWORKSPACE;
+  return hip_status(tv::launch_tree_attn(
+      q, k_pages, v_pages, seq_lens, parent, out, B, N, Hq, Hkv, D, 0, max_seq_len, scale,
+      dtype, plan, workspace, dev_status, static_cast<hipStream_t>(stream), block_table,
+      max_blocks, page_size, num_pages));
+}
+
+int tv_kv_compact_paged(void* k_pages, void* v_pages, const int32_t* block_table, int max_blocks,
+                        int page_size, int num_pages, int32_t* seq_lens, const int32_t* path,
+                        const int32_t* path_len, int B, int Hkv, int D, int P, int dtype,
+                        void* stream) {
+  if (!k_pages || !v_pages || !block_table || !seq_lens || !path || !path_len) return TV_EINVAL;
+  if (B < 1 || Hkv < 1 || D < 1 || P < 1 || max_blocks < 1 || num_pages < 1) return TV_EINVAL;
+  if (!page_size_ok(page_size)) return TV_EINVAL;
+  if ((long long)max_blocks * page_size > 2147483647LL) return TV_EINVAL;
+  if (!dtype_ok(dtype)) return TV_ENOTSUP;
+  const int esz = dtype == TV_F32 ? 4 : 2;
+  if ((D * esz) % 16 || P > 64 || (long long)P * D * esz > 65536) return TV_ENOTSUP;
+  if (B > 65535) return TV_ENOTSUP;
+  return hip_status(tv::launch_kv_compact(k_pages, v_pages, seq_lens, path, path_len, B, Hkv, D,
+                                          0, P, dtype, static_cast<hipStream_t>(stream),
+                                          block_table, max_blocks, page_size, num_pages));
 }
 
 size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype) {

@@ -69,6 +69,10 @@ struct AttnArgs {
   int nqblk, nsplit, chunk_len, total_blocks;
   int anc_words;   // ceil(N / 64)
   float scale_log2;  // scale * log2(e)
+  // paged caches (block_table != nullptr): pools [num_pages][Hkv][ps][D],
+  // logical row r of sequence b in page block_table[b][r >> page_shift]
+  const int32_t* block_table;
+  int max_blocks, page_shift, num_pages;
 };
 
 __device__ __forceinline__ void flag(int32_t* st, int b, int f) {
@@ -98,7 +102,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int D, int QBW, int NW>
+template <int D, int QBW, int NW, bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int kThreads = NW * 64;
@@ -118,6 +122,7 @@ void attn_bf16_kernel(AttnArgs a) {
   __shared__ unsigned long long sAnc[kMaxAncNodes * (TV_MAX_NODES / 64)];
   __shared__ unsigned sTreeMask;
   __shared__ int8_t sTreeList[TV_MAX_NODES / 64];
+  __shared__ int sBT[PAGED ? kMaxPagedBlocks : 1];  // this workgroup's pages
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -187,10 +192,42 @@ void attn_bf16_kernel(AttnArgs a) {
     // (published to the other threads by the first barrier of the tile loop)
   }
 
-  // ---- Q^T fragments of this lane's query columns
+  // ---- where key/value rows live: one contiguous plane per (sequence, KV
+  // head), or pages of a pool named by the block table.  For pages, the
+  // entries of the prefix chunk and of the tree rows are cached in LDS once
+  // (published by the first barrier of the tile loop).
   const size_t kv_plane = ((size_t)b * a.Hkv + g) * (size_t)a.Lcap * D;
-  const bf16_t* kp = a.k + kv_plane;
-  const bf16_t* vp = a.v + kv_plane;
+  const int sh = a.page_shift;
+  const int pre_blk0 = c0 >> sh;
+  const int n_pre_blk = PAGED && c1 > c0 ? ((c1 - 1) >> sh) - pre_blk0 + 1 : 0;
+  const int tree_blk0 = L >> sh;
+  if constexpr (PAGED) {
+    const int n_tree_blk = do_tree ? ((L + N - 1) >> sh) - tree_blk0 + 1 : 0;
+    const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
+    int bad = 0;
+    for (int i = tid; i < n_pre_blk + n_tree_blk; i += kThreads) {
+      const int blk = i < n_pre_blk ? pre_blk0 + i : tree_blk0 + (i - n_pre_blk);
+      int pg = bt[blk];
+      if (pg < 0 || pg >= a.num_pages) {
+        bad = 1;
+        pg = 0;
+      }
+      sBT[i] = pg;
+    }
+    if (bad) flag(a.dev_status, b, TV_STATUS_BAD_PAGE);
+  }
+  auto row_off = [&](int row, bool tree) -> size_t {
+    if constexpr (PAGED) {
+      const int blk = row >> sh;
+      const int pg = sBT[tree ? n_pre_blk + blk - tree_blk0 : blk - pre_blk0];
+      return ((((size_t)pg * a.Hkv + g) << sh) + (row & ((1 << sh) - 1))) * D;
+    } else {
+      (void)tree;
+      return kv_plane + (size_t)row * D;
+    }
+  };
+
+  // ---- Q^T fragments of this lane's query columns
   bf16x8_t qf[QBW][DS];
   int qnode[QBW];
   bool qvalid[QBW];
@@ -237,16 +274,16 @@ void attn_bf16_kernel(AttnArgs a) {
   };
 
   // Register staging of one tile: K pieces and V 4-key items.
-  uint4 kreg[KP];
-  uint4 vreg[VI][4];
-  auto load_tile = [&](int krow0, int nvalid) {
+  u32x4_t kreg[KP];
+  u32x4_t vreg[VI][4];
+  auto load_tile = [&](int krow0, int nvalid, bool tree) {
     const int last = krow0 + nvalid - 1;
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int c = min(tid + i * kThreads, KP_TOTAL - 1);
       const int r = c / (D / 8);
       const int x = c - r * (D / 8);
-      kreg[i] = *reinterpret_cast<const uint4*>(kp + (size_t)min(krow0 + r, last) * D + x * 8);
+      kreg[i] = *reinterpret_cast<const u32x4_t*>(a.k + row_off(min(krow0 + r, last), tree) + x * 8);
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
@@ -255,7 +292,7 @@ void attn_bf16_kernel(AttnArgs a) {
       const int x = c - kq * (D / 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        vreg[i][e] = *reinterpret_cast<const uint4*>(vp + (size_t)min(krow0 + kq * 4 + e, last) * D + x * 8);
+        vreg[i][e] = *reinterpret_cast<const u32x4_t*>(a.v + row_off(min(krow0 + kq * 4 + e, last), tree) + x * 8);
     }
   };
   auto store_tile = [&]() {
@@ -264,25 +301,23 @@ void attn_bf16_kernel(AttnArgs a) {
       const int c = min(tid + i * kThreads, KP_TOTAL - 1);
       const int r = c / (D / 8);
       const int x = c - r * (D / 8);
-      *reinterpret_cast<uint4*>(&sK[r * KROW + x * 8]) = kreg[i];
+      *reinterpret_cast<u32x4_t*>(&sK[r * KROW + x * 8]) = kreg[i];
     }
 #pragma unroll
     for (int i = 0; i < VI; ++i) {
       const int c = min(tid + i * kThreads, VI_TOTAL - 1);
       const int kq = c / (D / 8);
       const int x = c - kq * (D / 8);
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[i][0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[i][1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[i][2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[i][3]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int sh = (e & 1) * 16;
-        uint2 pk;
-        pk.x = ((w0[e >> 1] >> sh) & 0xffffu) | (((w1[e >> 1] >> sh) & 0xffffu) << 16);
-        pk.y = ((w2[e >> 1] >> sh) & 0xffffu) | (((w3[e >> 1] >> sh) & 0xffffu) << 16);
+        // element e of keys 4kq .. 4kq+3, packed as two bf16 pairs:
+        // v_perm picks the low (e even) or high (e odd) halves of two words
+        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x2_t pk;
+        pk.x = __builtin_amdgcn_perm(vreg[i][1][e >> 1], vreg[i][0][e >> 1], sel);
+        pk.y = __builtin_amdgcn_perm(vreg[i][3][e >> 1], vreg[i][2][e >> 1], sel);
         const int d = x * 8 + e;
-        *reinterpret_cast<uint2*>(&sVt[d * VROW + ((kq ^ vt_swz(d)) << 2)]) = pk;
+        *reinterpret_cast<u32x2_t*>(&sVt[d * VROW + ((kq ^ vt_swz(d)) << 2)]) = pk;
       }
     }
   };
@@ -296,7 +331,7 @@ void attn_bf16_kernel(AttnArgs a) {
     // Load the tile and stage it in LDS.  The loads are issued back to back
     // and are not held across the products: with two or more workgroups per
     // CU, one workgroup's loads overlap another's products.
-    load_tile(krow0, nvalid);
+    load_tile(krow0, nvalid, tree);
     store_tile();
     __syncthreads();  // this tile is in LDS
 
@@ -540,21 +575,20 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
 }
 
 // Variant table: (query rows per wavefront / 16, wavefronts per workgroup).
-template <int D>
-hipError_t launch_bf16(const AttnArgs& a, int qbw, int nw, hipStream_t stream) {
+template <int D, bool PAGED>
+hipError_t launch_bf16(const AttnArgs& a, int qbw, hipStream_t stream) {
   const dim3 grid(a.total_blocks);
-  if (qbw == 2 && nw == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4>), grid, dim3(256), 0, stream, a);
-  else if (qbw == 1 && nw == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4>), grid, dim3(256), 0, stream, a);
+  if (qbw == 2)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4, PAGED>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 2>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4, PAGED>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dtype) {
+AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dtype,
+                   int page_size) {
   AttnPlan p{};
   const int G = Hq / Hkv;
   const long R = (long)N * G;
@@ -592,6 +626,17 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dt
       p.nsplit = (ntiles + per - 1) / per;
     }
   }
+  if (dtype == TV_BF16 && page_size > 0 && ntiles > 0) {
+    // the block-table entries of one split and of the tree rows live in LDS
+    const int tree_blk = N / page_size + 2;
+    const long max_rows = (long)(kMaxPagedBlocks - tree_blk - 2) * page_size;
+    const long max_tiles = max_rows / kKT > 0 ? max_rows / kKT : 1;
+    if (p.chunk_len / kKT > max_tiles) {
+      const int per = (int)max_tiles;
+      p.chunk_len = per * kKT;
+      p.nsplit = (ntiles + per - 1) / per;
+    }
+  }
   p.ws_bytes = 0;
   if (p.nsplit > 1) {
     const size_t rows = (size_t)B * Hkv * p.nqblk * p.rows * p.nsplit;
@@ -604,7 +649,9 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* parent, void* out,
                             int B, int N, int Hq, int Hkv, int D, int Lcap,
                             int max_seq_len, float scale, int dtype, const AttnPlan& plan,
-                            void* ws, int32_t* dev_status, hipStream_t stream) {
+                            void* ws, int32_t* dev_status, hipStream_t stream,
+                            const int32_t* block_table, int max_blocks, int page_size,
+                            int num_pages) {
   if (dtype == TV_F32) {
     hipLaunchKernelGGL(attn_f32_kernel, dim3(N, Hq, B), dim3(256), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
@@ -635,13 +682,26 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
   a.total_blocks = B * Hkv * plan.nqblk * plan.nsplit;
   a.anc_words = (N + 63) / 64;
   a.scale_log2 = scale * kLog2e;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
+  a.page_shift = 0;
+  if (block_table != nullptr) {
+    while ((1 << a.page_shift) < page_size) ++a.page_shift;
+    a.Lcap = max_blocks << a.page_shift;  // logical capacity of a sequence
+  }
   if (plan.nsplit > 1) {
     const size_t rows = (size_t)B * Hkv * plan.nqblk * plan.rows * plan.nsplit;
     a.part_o = static_cast<float*>(ws);
     a.part_ml = static_cast<float*>(ws) + rows * D;
   }
-  hipError_t e = (D == 128) ? launch_bf16<128>(a, plan.qbw, plan.nw, stream)
-                            : launch_bf16<64>(a, plan.qbw, plan.nw, stream);
+  hipError_t e;
+  if (block_table != nullptr)
+    e = (D == 128) ? launch_bf16<128, true>(a, plan.qbw, stream)
+                   : launch_bf16<64, true>(a, plan.qbw, stream);
+  else
+    e = (D == 128) ? launch_bf16<128, false>(a, plan.qbw, stream)
+                   : launch_bf16<64, false>(a, plan.qbw, stream);
   if (e != hipSuccess || plan.nsplit == 1) return e;
   const size_t items = (size_t)B * Hkv * N * a.G * (D / 4);
   const dim3 grid((unsigned)((items + 255) / 256));

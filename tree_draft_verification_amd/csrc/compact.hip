@@ -6,6 +6,10 @@
 // uses its own offset (EQSPEC/EXSPEC abstract, arXiv 2510.22876 on the RSS
 // reader page: ragged acceptance must keep every sequence's KV state in step).
 //
+// Caches are contiguous planes [B][Hkv][Lcap][row] or pages of a pool
+// [num_pages][Hkv][page_size][row] named by a block table (row r of sequence
+// b in page block_table[b][r / page_size]); the moves are the same.
+//
 // One workgroup per sequence handles every plane (K and V of every KV head)
 // and then updates that sequence's length itself, so one launch does the
 // whole commit.  In-place hazard: move j reads row L+path[j], which move
@@ -22,10 +26,31 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kStageBytes = 64 * 1024;  // LDS staging per workgroup
 
+struct PagedArgs {
+  const int32_t* block_table;  // nullptr: contiguous planes
+  int max_blocks, page_shift, num_pages;
+};
+
+// Byte offset of row `row` of plane (b, head) in a cache, or -1 when a
+// paged entry is outside the pool.
+template <bool PAGED>
+__device__ __forceinline__ long long row_offset(const PagedArgs& pa, int b, int head, int Hkv,
+                                                int Lcap, int row, int row_bytes) {
+  if constexpr (PAGED) {
+    const int pg = pa.block_table[(size_t)b * pa.max_blocks + (row >> pa.page_shift)];
+    if (pg < 0 || pg >= pa.num_pages) return -1;
+    return ((((long long)pg * Hkv + head) << pa.page_shift) + (row & ((1 << pa.page_shift) - 1))) *
+           row_bytes;
+  } else {
+    return (((long long)b * Hkv + head) * Lcap + row) * row_bytes;
+  }
+}
+
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void compact_kernel(
     char* __restrict__ kc, char* __restrict__ vc, int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ path, const int32_t* __restrict__ path_len, int Hkv, int Lcap,
-    int P, int row_bytes) {
+    int P, int row_bytes, PagedArgs pa) {
   __shared__ uint4 stage[kStageBytes / 16];
   __shared__ int16_t s_move[64];  // j of every row that moves
   __shared__ int s_nmove;
@@ -60,10 +85,11 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
         const int rem = it - (it / per_plane) * per_plane;
         const int k = rem / chunks;
         const int x = rem - k * chunks;
-        const char* plane = (p < Hkv ? kc : vc) +
-                            ((size_t)b * Hkv + (p < Hkv ? p : p - Hkv)) * (size_t)Lcap * row_bytes;
         const int j = s_move[k];
-        stage[it] = reinterpret_cast<const uint4*>(plane + (size_t)(L + pth[j]) * row_bytes)[x];
+        const long long off =
+            row_offset<PAGED>(pa, b, p < Hkv ? p : p - Hkv, Hkv, Lcap, L + pth[j], row_bytes);
+        if (off >= 0)
+          stage[it] = reinterpret_cast<const uint4*>((p < Hkv ? kc : vc) + off)[x];
       }
       __syncthreads();
       for (int it = tid; it < items; it += kThreads) {
@@ -71,10 +97,12 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
         const int rem = it - (it / per_plane) * per_plane;
         const int k = rem / chunks;
         const int x = rem - k * chunks;
-        char* plane = (p < Hkv ? kc : vc) +
-                      ((size_t)b * Hkv + (p < Hkv ? p : p - Hkv)) * (size_t)Lcap * row_bytes;
         const int j = s_move[k];
-        reinterpret_cast<uint4*>(plane + (size_t)(L + j) * row_bytes)[x] = stage[it];
+        const int h = p < Hkv ? p : p - Hkv;
+        const long long src = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + pth[j], row_bytes);
+        const long long off = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + j, row_bytes);
+        if (off >= 0 && src >= 0)
+          reinterpret_cast<uint4*>((p < Hkv ? kc : vc) + off)[x] = stage[it];
       }
       __syncthreads();
     }
@@ -86,11 +114,21 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
 
 hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t* path,
                              const int32_t* path_len, int B, int Hkv, int D, int Lcap, int P,
-                             int dtype, hipStream_t stream) {
+                             int dtype, hipStream_t stream, const int32_t* block_table,
+                             int max_blocks, int page_size, int num_pages) {
   const int row_bytes = D * (dtype == TV_F32 ? 4 : 2);
-  hipLaunchKernelGGL(compact_kernel, dim3(B), dim3(kThreads), 0, stream,
-                     static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len, Hkv,
-                     Lcap, P, row_bytes);
+  PagedArgs pa{block_table, max_blocks, 0, num_pages};
+  if (block_table != nullptr) {
+    while ((1 << pa.page_shift) < page_size) ++pa.page_shift;
+    Lcap = max_blocks << pa.page_shift;
+    hipLaunchKernelGGL(compact_kernel<true>, dim3(B), dim3(kThreads), 0, stream,
+                       static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len,
+                       Hkv, Lcap, P, row_bytes, pa);
+  } else {
+    hipLaunchKernelGGL(compact_kernel<false>, dim3(B), dim3(kThreads), 0, stream,
+                       static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len,
+                       Hkv, Lcap, P, row_bytes, pa);
+  }
   return hipGetLastError();
 }
 

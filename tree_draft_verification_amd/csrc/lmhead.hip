@@ -119,13 +119,17 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
     wrow[vb] = W + (size_t)(v < V ? v : V - 1) * K + 32 * kg;
   }
   auto wload = [&](int c, int vb, int s) -> uint4 {
-    if constexpr (PACKED) {
-      // streamed once: non-temporal (measured 6% faster on the packed layout,
-      // slower on the row-major one)
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 t = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane)));
+    if constexpr (PACKED && MB == 4) {
+      // one row block (M <= 64): every W byte is read once, so the loads are
+      // non-temporal (measured 6% faster on the packed layout, slower on the
+      // row-major one)
+      const u32x4_t t = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane)));
       return make_uint4(t.x, t.y, t.z, t.w);
+    } else if constexpr (PACKED) {
+      // several row blocks share each W tile (neighbouring workgroups on one
+      // XCD): keep it cacheable so the re-reads hit L2
+      return *reinterpret_cast<const uint4*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane));
     } else {
       return *reinterpret_cast<const uint4*>(wrow[vb] + c * kKC + 8 * s);
     }

@@ -30,6 +30,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte register payload.  A native vector, not HIP's uint4 struct: arrays
+// of the struct are copied with memcpy and can stay in scratch memory.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 union Frag8 {  // eight bf16 values as one MFMA operand or one 16-byte load
   uint4 u;
@@ -81,14 +85,20 @@ struct AttnPlan {
   size_t ws_bytes;
 };
 
-AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dtype);
+// Block-table entries a tree-attention workgroup caches in LDS (paged caches).
+constexpr int kMaxPagedBlocks = 2048;
+
+// page_size 0 = contiguous caches
+AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dtype,
+                   int page_size);
 
 hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
                             const int32_t* seq_lens, const int32_t* parent,
                             void* out, int B, int N, int Hq, int Hkv, int D,
                             int Lcap, int max_seq_len, float scale, int dtype,
                             const AttnPlan& plan, void* ws, int32_t* dev_status,
-                            hipStream_t stream);
+                            hipStream_t stream, const int32_t* block_table = nullptr,
+                            int max_blocks = 0, int page_size = 0, int num_pages = 0);
 
 size_t lmhead_ws_bytes(int M, int K, int V, int dtype);
 size_t lmhead_packed_bytes(int V, int K);
@@ -106,6 +116,8 @@ hipError_t launch_tree_accept(const int32_t* parent, const int32_t* draft,
 
 hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t* path,
                              const int32_t* path_len, int B, int Hkv, int D,
-                             int Lcap, int P, int dtype, hipStream_t stream);
+                             int Lcap, int P, int dtype, hipStream_t stream,
+                             const int32_t* block_table = nullptr, int max_blocks = 0,
+                             int page_size = 0, int num_pages = 0);
 
 }  // namespace tv

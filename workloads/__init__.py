@@ -12,6 +12,7 @@ from .gen import (  # noqa: F401
     draft_coins,
     draft_tokens,
     lmhead_inputs,
+    paged_layout,
     bf16_bits_from_f32,
     BF16_QNAN,
 )

@@ -325,3 +325,31 @@ def draft_tokens(parent: np.ndarray, coins: dict, tgt: np.ndarray) -> np.ndarray
     tok = np.where(copy, at_parent, coins["rand_tok"]).astype(np.int32)
     tok[:, 0] = coins["rand_tok"][:, 0]
     return tok
+
+
+def paged_layout(k_cache, v_cache, page_size: int, seed: int, extra_pages: int = 3) -> dict:
+    """The same caches laid out in pages of a shared pool.
+
+    Every sequence's logical rows 0..Lcap-1 are cut into blocks of
+    page_size rows (ceil(Lcap / page_size) blocks); the blocks of all sequences are placed on pages chosen by
+    a seeded random permutation of the pool, which also holds extra_pages
+    unused pages filled with NaN.  Pool layout [num_pages][Hkv][page_size][D].
+    """
+    k_cache = np.asarray(k_cache)
+    B, Hkv, Lcap, D = k_cache.shape
+    nblk = -(-Lcap // page_size)      # a partial last block is padded with NaN rows
+    num_pages = B * nblk + extra_pages
+    perm = np.random.default_rng(seed).permutation(num_pages)
+    block_table = perm[:B * nblk].reshape(B, nblk).astype(np.int32)
+    nan = BF16_QNAN if k_cache.dtype == np.uint16 else np.float32(np.nan)
+    pools = []
+    for cache in (k_cache, np.asarray(v_cache)):
+        pool = np.full((num_pages, Hkv, page_size, D), nan, dtype=cache.dtype)
+        if nblk * page_size != Lcap:
+            pad = np.full((B, Hkv, nblk * page_size - Lcap, D), nan, dtype=cache.dtype)
+            cache = np.concatenate([cache, pad], axis=2)
+        blocks = cache.reshape(B, Hkv, nblk, page_size, D).transpose(0, 2, 1, 3, 4)
+        pool[block_table.reshape(-1)] = blocks.reshape(B * nblk, Hkv, page_size, D)
+        pools.append(pool)
+    return dict(k_pages=pools[0], v_pages=pools[1], block_table=block_table,
+                page_size=page_size, num_pages=num_pages)
