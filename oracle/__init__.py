@@ -29,3 +29,11 @@ from .verify import (  # noqa: F401
     tree_attention_paged,
     verify_step,
 )
+from .model import (  # noqa: F401
+    kv_compact_layers,
+    node_positions,
+    rms_norm,
+    rope,
+    silu,
+    verify_pass,
+)

@@ -22,13 +22,14 @@ import numpy as np
 # input decoding
 
 def decode(x, dtype: str) -> np.ndarray:
-    """Exact fp64 value of stored inputs: bf16 bit patterns (uint16) or fp32."""
+    """Exact fp64 value of stored inputs: bf16 bit patterns (uint16), fp32, or
+    values already in fp64 (dtype "f64")."""
     x = np.asarray(x)
     if dtype == "bf16":
         if x.dtype != np.uint16:
             raise TypeError("bf16 inputs are expected as uint16 bit patterns")
         return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    if dtype == "f32":
+    if dtype in ("f32", "f64"):
         return x.astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")
 

@@ -16,3 +16,4 @@ from .gen import (  # noqa: F401
     bf16_bits_from_f32,
     BF16_QNAN,
 )
+from .model import MODELS, ModelConfig, model_inputs, model_weights  # noqa: F401
