@@ -10,10 +10,13 @@ LM head, whose per-launch time is taken with HIP events on the launch
 stream), and the fp64 oracle timed on this host's cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--paged PAGE_SIZE]
+                    [--paged PAGE_SIZE] [--model qwen3_8b]
 
 --paged keeps the key/value caches in pages of a shared pool (placed by a
 seeded random permutation) and runs the paged attention and compaction calls.
+--model runs the whole multi-layer verification step instead (36 Qwen3-8B-
+shaped layers with synthetic weights, LM head, acceptance, one compaction
+launch for every layer), captured once as a graph and replayed.
 """
 from __future__ import annotations
 
@@ -130,6 +133,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paged", type=int, default=0,
                     help="page size of a paged key/value cache (0: contiguous caches)")
+    ap.add_argument("--model", default=None,
+                    help="time the multi-layer pass of this synthetic model (e.g. qwen3_8b)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many bytes")
     args = ap.parse_args()
@@ -139,6 +144,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         copy_calibration(args.calibrate_copy)
+        return
+    if args.model:
+        model_bench(args)
         return
 
     import torch
@@ -297,6 +305,177 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, a, lm, coins)
+    print(json.dumps(res), flush=True)
+
+
+def model_work(cfg, wl, seq_lens) -> dict:
+    """Algorithmic HBM bytes and flops of one multi-layer pass: every weight
+    read once, the prefix K/V of every layer read once, the tree rows and the
+    activations between kernels (bf16 in, fp32 partial sums excluded: they
+    are an implementation choice)."""
+    Hd, I, Ly = cfg.hidden, cfg.inter, cfg.layers
+    qkv = (cfg.Hq + 2 * cfg.Hkv) * cfg.D
+    M = wl.B * wl.N
+    w_layer = 2 * (qkv * Hd + Hd * cfg.Hq * cfg.D + 2 * I * Hd + Hd * I) + 2 * (2 * Hd + 2 * cfg.D)
+    weights = Ly * w_layer + 2 * cfg.V * Hd + 2 * Hd + 2 * M * Hd
+    kv = Ly * (2 * int(np.sum(seq_lens)) * cfg.Hkv * cfg.D * 2 + 2 * M * cfg.Hkv * cfg.D * 2)
+    flops = 2 * M * (Ly * (qkv * Hd + Hd * cfg.Hq * cfg.D + 3 * I * Hd) + cfg.V * Hd)
+    return dict(bytes=int(weights + kv), weight_bytes=int(weights), kv_bytes=int(kv),
+                flops=int(flops))
+
+
+_LAYER_KEYS = ("ln1", "w_qkv", "q_norm", "k_norm", "w_o", "ln2", "w_gu", "w_down")
+
+
+def model_cpu_baseline(cfg, wl, w):
+    """The fp64 oracle's pass on a bounded sample: the pass with one and with
+    two of the model's layers (the rest of the pass unchanged), timed, and
+    scaled to all layers: t = t1 + (t2 - t1) * (layers - 1)."""
+    import oracle
+    from workloads import model_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    xs = model_inputs(cfg, wl, layers=2)
+    t = {}
+    for n in (1, 2):
+        wn = {k: (v[:n] if k in _LAYER_KEYS else v) for k, v in w.items()}
+        t0 = time.perf_counter()
+        oracle.verify_pass(cfg.dims(layers=n), wn, xs["tokens"], xs["parent"], xs["seq_lens"],
+                           xs["k_cache"][:n], xs["v_cache"][:n], logit_rows=[0])
+        t[n] = time.perf_counter() - t0
+    t_pass = t[1] + max(t[2] - t[1], 0.0) * (cfg.layers - 1)
+    M = wl.B * wl.N
+    return dict(value=round(M / t_pass, 4), unit="nodes/s", cores=int(cores), kind="oracle",
+                sample=f"fp64 oracle pass over {wl.name} with 1 and 2 of {cfg.layers} layers "
+                       f"({t[1] + t[2]:.1f} s), scaled to {cfg.layers} layers")
+
+
+def model_bench(args):
+    import torch
+
+    import tree_draft_verification_amd as tv
+    from workloads import (MODELS, WORKLOADS, draft_coins, draft_tokens, model_inputs,
+                           model_weights)
+
+    cfg = MODELS[args.model]
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+
+    def progress(msg):
+        print(f"[bench] {time.perf_counter() - t_setup:6.1f} s  {msg}", file=sys.stderr, flush=True)
+
+    w = model_weights(cfg)
+    x = model_inputs(cfg, wl)
+    progress("synthetic weights and caches drawn")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    model = tv.tv_model_pack(cfg.dims(), {k: bf(v) for k, v in w.items()})
+    torch.cuda.synchronize()
+    progress("weights packed on the device")
+    k0, v0 = bf(x["k_cache"]), bf(x["v_cache"])
+    k, v = k0.clone(), v0.clone()
+    lens0 = i32(x["seq_lens"])
+    lens = lens0.clone()
+    parent = i32(x["parent"])
+    msl = int(x["seq_lens"].max())
+    M, P = wl.B * wl.N, 32
+    arg = torch.empty(M, dtype=torch.int32, device=dev)
+    path = torch.empty((wl.B, P), dtype=torch.int32, device=dev)
+    plen = torch.empty(wl.B, dtype=torch.int32, device=dev)
+    bonus = torch.empty(wl.B, dtype=torch.int32, device=dev)
+    ws = torch.zeros(tv.tv_verify_pass_workspace(model, wl.B, wl.N, msl), dtype=torch.uint8,
+                     device=dev)
+    cws = torch.zeros(tv.tv_kv_compact_layers_workspace(wl.B), dtype=torch.uint8, device=dev)
+    # The simulated drafter copies the target's greedy token at the parent
+    # with the workload's probability; the target's tokens come from passes
+    # of this model, one tree level settled per pass (setup, untimed).
+    coins = draft_coins(wl, x["depth"])
+    tok_h = x["tokens"].copy()
+    for _ in range(int(x["depth"].max()) + 1):
+        tokens = i32(tok_h)
+        tv.tv_verify_pass(model, tokens, parent, lens0, k, v, arg, max_seq_len=msl, workspace=ws)
+        new = draft_tokens(x["parent"], coins, arg.cpu().numpy().reshape(wl.B, wl.N))
+        if (new == tok_h).all():
+            break
+        tok_h = new
+    tokens = i32(tok_h)
+    progress("draft tokens settled")
+
+    def step():
+        lens.copy_(lens0)   # compaction advanced the lengths; restore the batch
+        tv.tv_verify_pass(model, tokens, parent, lens, k, v, arg, max_seq_len=msl, workspace=ws)
+        tv.tv_tree_accept(parent, tokens, arg, P, path=path, path_len=plen, bonus=bonus)
+        tv.tv_kv_compact_layers(k, v, lens, path, plen, workspace=cws)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+        s.synchronize()
+        # eager step time (the same calls, launched one by one)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(5):
+            step()
+        e1.record(s)
+        s.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / 5
+        tv.tv_graph_begin(s)
+        step()
+        graph = tv.tv_graph_end(s)
+        for _ in range(args.warmup):
+            graph.launch(s)
+        s.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        for i in range(args.steps):
+            ev[i][0].record(s)
+            graph.launch(s)
+            ev[i][1].record(s)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in ev])
+    step_us = float(np.median(per))
+    value = M * args.steps / (t1 - t0)
+    plen_h = plen.cpu().numpy()
+    work = model_work(cfg, wl, x["seq_lens"])
+    achieved = work["bytes"] / (step_us * 1e-6) / 1e9
+    res = {
+        "metric": "verified tree nodes/s, whole multi-layer verification step (graph replay)",
+        "value": round(value, 1), "unit": "nodes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded weights and caches, simulated drafter)",
+        "config": {"workload": f"{cfg.name} x {wl.name}", "layers": cfg.layers,
+                   "hidden": cfg.hidden, "inter": cfg.inter, "batch": wl.B, "nodes": wl.N,
+                   "prefix": [int(t) for t in x["seq_lens"]], "parallelism": "none (1 GPU)"},
+        "step_us": round(step_us, 2),
+        "step_us_p10_p90": [round(float(np.percentile(per, 10)), 2),
+                            round(float(np.percentile(per, 90)), 2)],
+        "eager_step_us": round(eager_us, 2),
+        "mean_path_len": float(plen_h.mean()),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole step (graph): weights + KV streamed once",
+                     "algorithmic_bytes": work["bytes"], "launch_us": round(step_us, 2)},
+        "work": work,
+        "setup_s": round(setup_s, 1),
+    }
+    progress("timed")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = model_cpu_baseline(cfg, wl, w)
+        progress("cpu baseline timed")
     print(json.dumps(res), flush=True)
 
 

@@ -57,6 +57,7 @@ extern "C" {
 #define TV_STATUS_BAD_LEN    2 /* L_b < 0, L_b > max_seq_len or L_b+N > Lcap */
 #define TV_STATUS_DEPTH      4 /* accepted path longer than P                */
 #define TV_STATUS_BAD_PAGE   8 /* a block-table entry outside [0, num_pages) */
+#define TV_STATUS_BAD_TOKEN 16 /* a draft token outside [0, vocab)           */
 
 #define TV_MAX_NODES 1024 /* N limit of every call                           */
 
@@ -222,6 +223,109 @@ int tv_kv_compact_paged(void* k_pages, void* v_pages, const int32_t* block_table
                         int32_t* seq_lens, const int32_t* path,
                         const int32_t* path_len, int B, int Hkv, int D, int P,
                         int dtype, void* stream);
+
+/*
+ * Multi-layer verification pass: the target model run over every node of
+ * the draft trees in one pass, ending in the LM-head argmax (JetSpec GitHub
+ * README, "JetSpec > Overview": one forward pass of the target under the
+ * tree-causal mask; its "Quick Start" compiles that verification and
+ * replays it as a graph; the JetSpec abstract names dense and MoE Qwen3
+ * targets).  The model is a dense Qwen3-style decoder stack (pre-norm
+ * RMSNorm, grouped-query attention with per-head RMSNorm of queries and keys
+ * before rotary embedding, SwiGLU MLP).  Node i of sequence b is token
+ * tokens[b][i] at position L_b + depth(i); its key and value rows go to row
+ * L_b + i of every layer's cache, and it attends as in tv_tree_verify_attn.
+ *
+ * dims     host struct: layers, hidden, Hq, Hkv, D, inter (MLP width),
+ *          vocab, rms_eps, rope_theta (rotary pairs (d, d + D/2) turned by
+ *          pos * rope_theta^(-2d/D))
+ * weights  host struct of device pointers, all bf16:
+ *            embed      [vocab][hidden] row-major
+ *            ln1, ln2   [layers][hidden]
+ *            q_norm, k_norm [layers][D]
+ *            w_qkv      layers x packed([(Hq + 2 Hkv) D] rows, K = hidden):
+ *                       q rows (head-major), then k rows, then v rows
+ *            w_o        layers x packed([hidden] rows, K = Hq D)
+ *            w_gu       layers x packed([2 inter] rows, K = hidden): gate
+ *                       rows, then up rows
+ *            w_down     layers x packed([hidden] rows, K = inter)
+ *            final_norm [hidden]
+ *            lm_head    packed([vocab] rows, K = hidden)
+ *          "packed(r, K)" is the tv_lmhead_pack_weights layout of an [r][K]
+ *          row-major weight, tv_lmhead_packed_bytes(r, K, TV_BF16) bytes;
+ *          the layers' blocks follow each other without gaps.
+ * tokens, parent  [B][N] int32; seq_lens [B] (read only: the caller runs
+ *          tv_tree_accept and tv_kv_compact_layers afterwards)
+ * k_cache, v_cache  [layers][B][Hkv][Lcap][D] bf16: prefix rows read, tree
+ *          rows L_b .. L_b+N-1 written
+ * argmax   [B*N] int32, row b*N + i
+ * logits   [B*N][vocab] fp32 or NULL (for checking; not on the hot path)
+ * hidden_out [B*N][hidden] fp32 or NULL: the final normalised hidden states
+ * workspace  tv_verify_pass_workspace() bytes, zero-filled before its first
+ *          use; the pass leaves its first part zero again (the LM-head
+ *          contract), so a buffer serves any number of passes in stream
+ *          order.  Nothing is allocated or memset: the pass may be captured
+ *          with tv_graph_begin/tv_graph_end.
+ * Supported: D in {64, 128}; hidden, inter and Hq*D multiples of 256;
+ *          hidden <= 16384; 1 <= N <= TV_MAX_NODES.  Device-side checks: TV_STATUS_BAD_PARENT,
+ *          TV_STATUS_BAD_LEN, TV_STATUS_BAD_TOKEN (the token is read as 0).
+ */
+typedef struct {
+  int layers, hidden, Hq, Hkv, D, inter, vocab;
+  float rms_eps, rope_theta;
+} tv_model_dims;
+
+typedef struct {
+  const void* embed;
+  const void* ln1;
+  const void* w_qkv;
+  const void* q_norm;
+  const void* k_norm;
+  const void* w_o;
+  const void* ln2;
+  const void* w_gu;
+  const void* w_down;
+  const void* final_norm;
+  const void* lm_head;
+} tv_model_weights;
+
+size_t tv_verify_pass_workspace(const tv_model_dims* dims, int B, int N, int max_seq_len);
+int tv_verify_pass(const tv_model_dims* dims, const tv_model_weights* weights,
+                   const int32_t* tokens, const int32_t* parent,
+                   const int32_t* seq_lens, void* k_cache, void* v_cache, int B,
+                   int N, int Lcap, int max_seq_len, int32_t* argmax,
+                   float* logits, float* hidden_out, void* workspace,
+                   size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/*
+ * KV compaction of every layer in one launch: the row moves of
+ * tv_kv_compact applied to caches [layers][B][Hkv][Lcap][D], then
+ * seq_lens[b] += path_len[b] once.  The workgroups of a sequence share its
+ * planes; the last of them to finish updates the length through a counter in
+ * `workspace` (tv_kv_compact_layers_workspace() bytes, zero-filled before
+ * its first use and left zero by every call).
+ */
+size_t tv_kv_compact_layers_workspace(int B);
+int tv_kv_compact_layers(void* k_cache, void* v_cache, int32_t* seq_lens,
+                         const int32_t* path, const int32_t* path_len, int B,
+                         int Hkv, int D, int Lcap, int P, int layers, int dtype,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Graph capture of a sequence of calls (the README's "Quick Start" engine
+ * replays verification as a graph).  tv_graph_begin starts capturing the
+ * work later enqueued on `stream` (a stream created by the caller, not the
+ * null stream); tv_graph_end stops, instantiates the captured work and
+ * returns it in *graph (owned by the caller, freed with tv_graph_destroy).
+ * tv_graph_launch replays it on a stream: the same kernels with the same
+ * pointers, reading whatever the buffers hold at that time.  Between begin
+ * and end the thread must not allocate or synchronise device memory.
+ */
+typedef struct tv_graph tv_graph;
+int tv_graph_begin(void* stream);
+int tv_graph_end(void* stream, tv_graph** graph);
+int tv_graph_launch(const tv_graph* graph, void* stream);
+int tv_graph_destroy(tv_graph* graph);
 
 /* Text of a status code (TV_EHIP: the HIP error text of the failed launch). */
 const char* tv_status_string(int status);

@@ -41,7 +41,10 @@ def test_header_declares_the_four_calls():
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
-              "tv_kv_compact_paged", "tv_status_string", "tv_abi_version"):
+              "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
+              "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
+              "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_status_string",
+              "tv_abi_version"):
         assert n in names
 
 
@@ -174,12 +177,59 @@ def test_paged_host_validation(lib):
     assert c(FAKE, FAKE, FAKE, 68, 16, 100, FAKE, FAKE, FAKE, 1, 8, 128, 65, 0, None) == -2
 
 
+def _pass(lib, dims=None, weights=None, **kw):
+    from tree_draft_verification_amd import _lib
+    d = dims or _lib.ModelDims(2, 256, 4, 2, 64, 512, 1000, 1e-6, 1e6)
+    w = weights or _lib.ModelWeights(*([0x1000] * 11))
+    a = dict(tok=FAKE, par=FAKE, sl=FAKE, k=FAKE, v=FAKE, B=2, N=12, Lcap=128, msl=100,
+             arg=FAKE, lg=None, hid=None, ws=FAKE, wsb=1 << 30, st=None, stream=None)
+    a.update(kw)
+    return lib.tv_verify_pass(ctypes.byref(d), ctypes.byref(w), a["tok"], a["par"], a["sl"],
+                              a["k"], a["v"], a["B"], a["N"], a["Lcap"], a["msl"], a["arg"],
+                              a["lg"], a["hid"], a["ws"], a["wsb"], a["st"], a["stream"])
+
+
+def test_pass_host_validation(lib):
+    from tree_draft_verification_amd import _lib
+    D = _lib.ModelDims
+    d = D(2, 256, 4, 2, 64, 512, 1000, 1e-6, 1e6)
+    need = lib.tv_verify_pass_workspace(ctypes.byref(d), 2, 12, 100)
+    assert need > 0
+    assert _pass(lib, tok=None) == -1
+    assert _pass(lib, weights=_lib.ModelWeights(*([0x1000] * 10 + [0]))) == -1  # lm_head NULL
+    assert _pass(lib, msl=120) == -1                      # max_seq_len + N > Lcap
+    assert _pass(lib, dims=D(2, 256, 3, 2, 64, 512, 1000, 1e-6, 1e6)) == -1    # Hq % Hkv
+    assert _pass(lib, dims=D(2, 256, 4, 2, 64, 512, 1000, 1e-6, 1.0)) == -1    # rope_theta
+    assert _pass(lib, dims=D(2, 256, 4, 2, 96, 512, 1000, 1e-6, 1e6)) == -2    # D
+    assert _pass(lib, dims=D(2, 320, 4, 2, 64, 512, 1000, 1e-6, 1e6)) == -2    # hidden % 256
+    assert _pass(lib, dims=D(2, 256, 4, 2, 64, 640, 1000, 1e-6, 1e6)) == -2    # inter % 256
+    assert _pass(lib, N=1025, Lcap=2048) == -2
+    assert _pass(lib, ws=None) == -3
+    assert _pass(lib, wsb=need - 1) == -3
+    c = lib.tv_kv_compact_layers
+    cw = lib.tv_kv_compact_layers_workspace(3)
+    assert cw >= 12
+    assert c(None, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 36, 0, FAKE, cw, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 0, 0, FAKE, cw, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 65, 36, 0, FAKE, cw, None) == -2
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 36, 0, None, cw, None) == -3
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 36, 0, FAKE, cw - 1, None) == -3
+    # graphs: the null stream cannot be captured; null handles are rejected
+    assert lib.tv_graph_begin(None) == -1
+    assert lib.tv_graph_end(None, None) == -1
+    assert lib.tv_graph_launch(None, None) == -1
+    assert lib.tv_graph_destroy(None) == -1
+
+
 def test_binding_names_match_the_c_calls():
     import tree_draft_verification_amd as tv
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
-              "tv_kv_compact_paged", "tv_status_string", "tv_abi_version"):
+              "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
+              "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
+              "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_status_string",
+              "tv_abi_version"):
         assert callable(getattr(tv, n))
     assert tv.tv_status_string(-3) == "workspace missing or too small"

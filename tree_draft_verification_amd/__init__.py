@@ -16,6 +16,7 @@ One verification step (JetSpec GitHub README, "JetSpec > Overview"):
 """
 from __future__ import annotations
 
+import ctypes
 import math
 
 import torch
@@ -23,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import (TV_BF16, TV_F32, TV_LAYOUT_PACKED, TV_LAYOUT_ROWMAJOR,  # noqa: F401
                    TV_MAX_NODES, TV_STATUS_BAD_LEN, TV_STATUS_BAD_PAGE, TV_STATUS_BAD_PARENT,
-                   TV_STATUS_DEPTH)
+                   TV_STATUS_BAD_TOKEN, TV_STATUS_DEPTH)
 
 _LIB_HANDLE = None
 
@@ -40,6 +41,10 @@ __all__ = [
     "tv_lmhead_argmax", "tv_lmhead_argmax_workspace", "tv_lmhead_packed_bytes",
     "tv_lmhead_pack_weights", "PackedWeights", "tv_tree_accept",
     "tv_kv_compact", "tv_status_string", "tv_abi_version", "library_path",
+    "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace", "tv_kv_compact_paged",
+    "Model", "tv_model_pack", "tv_verify_pass", "tv_verify_pass_workspace",
+    "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "Graph", "tv_graph_begin",
+    "tv_graph_end", "tv_graph_launch", "tv_graph_destroy",
 ]
 
 
@@ -317,3 +322,165 @@ def tv_kv_compact_paged(k_pages, v_pages, block_table, seq_lens, path, path_len)
         _ptr(k_pages), _ptr(v_pages), _ptr(block_table), max_blocks, page_size, num_pages,
         _ptr(seq_lens), _ptr(path), _ptr(path_len), B, Hkv, D, P, dt, _stream(k_pages.device))
     _check("tv_kv_compact_paged", st)
+
+
+# ---------------------------------------------------------------- multi-layer pass
+
+_PACKED = ("w_qkv", "w_o", "w_gu", "w_down")
+
+
+class Model:
+    """Device-resident weights of a decoder stack in the layout tv_verify_pass
+    reads (see tv_model_pack); holds the buffers the C structs point to."""
+
+    def __init__(self, dims: dict, bufs: dict):
+        self.dims = dict(dims)
+        self.bufs = bufs
+        self.c_dims = _lib.ModelDims(dims["layers"], dims["hidden"], dims["Hq"], dims["Hkv"],
+                                     dims["D"], dims["inter"], dims["V"], dims["eps"],
+                                     dims["theta"])
+        self.c_weights = _lib.ModelWeights(*[bufs[n].data_ptr() for n, _ in
+                                             _lib.ModelWeights._fields_])
+        self.device = bufs["embed"].device
+
+
+def tv_model_pack(dims: dict, w: dict) -> Model:
+    """Stack a model's bf16 device weights for tv_verify_pass.
+
+    dims: layers, hidden, Hq, Hkv, D, inter, V, eps, theta.  w: bf16 tensors
+    embed [V,hidden], ln1/ln2 [layers,hidden], q_norm/k_norm [layers,D],
+    w_qkv [layers,(Hq+2Hkv)D,hidden], w_o [layers,hidden,Hq D],
+    w_gu [layers,2 inter,hidden], w_down [layers,hidden,inter],
+    final_norm [hidden], lm_head [V,hidden].  Each projection of each layer is
+    repacked with tv_lmhead_pack_weights into one buffer per projection.
+    """
+    bufs = {k: w[k].contiguous() for k in ("embed", "ln1", "ln2", "q_norm", "k_norm",
+                                            "final_norm")}
+    for k in _PACKED:
+        t = w[k]
+        Ly, R, K = t.shape
+        per = tv_lmhead_packed_bytes(R, K, TV_BF16)
+        if per == 0:
+            raise TreeVerifyError("tv_model_pack", _lib.TV_ENOTSUP)
+        out = torch.empty(Ly * per, dtype=torch.uint8, device=t.device)
+        for ly in range(Ly):
+            src = t[ly].contiguous()
+            st = _lib_handle().tv_lmhead_pack_weights(_ptr(src), out.data_ptr() + ly * per, R, K,
+                                                      TV_BF16, _stream(t.device))
+            _check("tv_lmhead_pack_weights", st)
+        bufs[k] = out
+    bufs["lm_head"] = tv_lmhead_pack_weights(w["lm_head"]).data
+    return Model(dims, bufs)
+
+
+def tv_verify_pass_workspace(model: Model, B: int, N: int, max_seq_len: int) -> int:
+    return int(_lib_handle().tv_verify_pass_workspace(model.c_dims, B, N, max_seq_len))
+
+
+def tv_verify_pass(model: Model, tokens, parent, seq_lens, k_cache, v_cache, argmax=None, *,
+                   max_seq_len: int, logits=None, hidden_out=None, workspace=None,
+                   dev_status=None) -> torch.Tensor:
+    """The multi-layer pass; caches [layers,B,Hkv,Lcap,D] bf16.  Returns argmax [B*N]."""
+    B, N = tokens.shape
+    d = model.dims
+    Ly, Bk, Hkv, Lcap, D = k_cache.shape
+    if (Ly, Bk, Hkv, D) != (d["layers"], B, d["Hkv"], d["D"]) or v_cache.shape != k_cache.shape:
+        raise ValueError("caches do not match the model and batch")
+    if k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise TypeError("caches must be bfloat16")
+    _i32(tokens, (B, N), "tokens")
+    _i32(parent, (B, N), "parent")
+    _i32(seq_lens, (B,), "seq_lens")
+    M = B * N
+    dev = tokens.device
+    if argmax is None:
+        argmax = torch.empty(M, dtype=torch.int32, device=dev)
+    _i32(argmax, (M,), "argmax")
+    if logits is not None and (logits.dtype != torch.float32
+                               or tuple(logits.shape) != (M, d["V"])):
+        raise ValueError("logits must be float32 of shape (B*N, V)")
+    if hidden_out is not None and (hidden_out.dtype != torch.float32
+                                   or tuple(hidden_out.shape) != (M, d["hidden"])):
+        raise ValueError("hidden_out must be float32 of shape (B*N, hidden)")
+    need = tv_verify_pass_workspace(model, B, N, max_seq_len)
+    if workspace is None:
+        workspace = _cached_workspace("pass", need, dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib_handle().tv_verify_pass(
+        ctypes.byref(model.c_dims), ctypes.byref(model.c_weights), _ptr(tokens), _ptr(parent),
+        _ptr(seq_lens), _ptr(k_cache), _ptr(v_cache), B, N, Lcap, int(max_seq_len),
+        _ptr(argmax), _ptr(logits), _ptr(hidden_out), _ptr(workspace), ws_bytes,
+        _ptr(dev_status), _stream(dev))
+    _check("tv_verify_pass", st)
+    return argmax
+
+
+def tv_kv_compact_layers_workspace(B: int) -> int:
+    return int(_lib_handle().tv_kv_compact_layers_workspace(B))
+
+
+def tv_kv_compact_layers(k_cache, v_cache, seq_lens, path, path_len, *, workspace=None) -> None:
+    """tv_kv_compact on every layer of [layers,B,Hkv,Lcap,D] caches in one launch."""
+    Ly, B, Hkv, Lcap, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache disagree")
+    dt = _dtype_code(k_cache)
+    _i32(seq_lens, (B,), "seq_lens")
+    P = path.shape[1]
+    _i32(path, (B, P), "path")
+    _i32(path_len, (B,), "path_len")
+    need = tv_kv_compact_layers_workspace(B)
+    if workspace is None:
+        workspace = _cached_workspace("compact_layers", need, k_cache.device)
+    st = _lib_handle().tv_kv_compact_layers(
+        _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(path), _ptr(path_len), B, Hkv, D, Lcap,
+        P, Ly, dt, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(k_cache.device))
+    _check("tv_kv_compact_layers", st)
+
+
+# ---------------------------------------------------------------- graphs
+
+class Graph:
+    """A captured and instantiated sequence of calls (tv_graph_end)."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def launch(self, stream=None):
+        tv_graph_launch(self, stream)
+
+    def __del__(self):
+        if getattr(self, "handle", None):
+            try:
+                tv_graph_destroy(self)
+            except Exception:  # pragma: no cover - interpreter shutdown
+                pass
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def tv_graph_begin(stream) -> None:
+    """Start capturing the calls enqueued on ``stream`` (a torch.cuda.Stream
+    other than the default one)."""
+    _check("tv_graph_begin", _lib_handle().tv_graph_begin(_stream_handle(stream)))
+
+
+def tv_graph_end(stream) -> Graph:
+    out = ctypes.c_void_p()
+    _check("tv_graph_end", _lib_handle().tv_graph_end(_stream_handle(stream), ctypes.byref(out)))
+    return Graph(out.value)
+
+
+def tv_graph_launch(graph: Graph, stream=None) -> None:
+    _check("tv_graph_launch", _lib_handle().tv_graph_launch(graph.handle, _stream_handle(stream)))
+
+
+def tv_graph_destroy(graph: Graph) -> None:
+    h, graph.handle = graph.handle, None
+    if h:
+        _check("tv_graph_destroy", _lib_handle().tv_graph_destroy(h))

@@ -184,3 +184,123 @@ int tv_kv_compact(void* k_cache, void* v_cache, int32_t* seq_lens, const int32_t
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- multi-layer pass
+
+namespace {
+
+// 0 when the dims are usable, else the status to return.
+int dims_status(const tv_model_dims* d) {
+  if (!d) return TV_EINVAL;
+  if (d->layers < 1 || d->hidden < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1 || d->inter < 1 ||
+      d->vocab < 1 || d->Hq % d->Hkv)
+    return TV_EINVAL;
+  if (!isfinite(d->rms_eps) || d->rms_eps < 0.f || !isfinite(d->rope_theta) ||
+      d->rope_theta <= 1.f)
+    return TV_EINVAL;
+  if (d->D != 64 && d->D != 128) return TV_ENOTSUP;
+  if (d->hidden % 256 || d->inter % 256 || (d->Hq * d->D) % 256) return TV_ENOTSUP;
+  if (d->hidden > 16384) return TV_ENOTSUP;  // one row per norm workgroup
+  if ((long long)d->vocab * d->hidden > (1LL << 40)) return TV_ENOTSUP;
+  return TV_OK;
+}
+
+bool weights_ok(const tv_model_weights* w) {
+  return w && w->embed && w->ln1 && w->w_qkv && w->q_norm && w->k_norm && w->w_o && w->ln2 &&
+         w->w_gu && w->w_down && w->final_norm && w->lm_head;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tv_verify_pass_workspace(const tv_model_dims* dims, int B, int N, int max_seq_len) {
+  if (dims_status(dims) != TV_OK || B < 1 || N < 1 || N > TV_MAX_NODES || max_seq_len < 0 ||
+      (long long)B * N > 65536)
+    return 0;
+  return tv::pass_plan(*dims, B, N, max_seq_len).ws_bytes;
+}
+
+int tv_verify_pass(const tv_model_dims* dims, const tv_model_weights* weights,
+                   const int32_t* tokens, const int32_t* parent, const int32_t* seq_lens,
+                   void* k_cache, void* v_cache, int B, int N, int Lcap, int max_seq_len,
+                   int32_t* argmax, float* logits, float* hidden_out, void* workspace,
+                   size_t ws_bytes, int32_t* dev_status, void* stream) {
+  const int ds = dims_status(dims);
+  if (ds != TV_OK) return ds;
+  if (!weights_ok(weights) || !tokens || !parent || !seq_lens || !k_cache || !v_cache ||
+      !argmax)
+    return TV_EINVAL;
+  if (B < 1 || N < 1 || max_seq_len < 0 || Lcap < 1) return TV_EINVAL;
+  if ((long long)max_seq_len + N > Lcap) return TV_EINVAL;
+  if (N > TV_MAX_NODES || (long long)B * N > 65536) return TV_ENOTSUP;
+  if ((long long)dims->layers * B * dims->Hkv * Lcap * dims->D > (1LL << 40)) return TV_ENOTSUP;
+  const tv::PassPlan plan = tv::pass_plan(*dims, B, N, max_seq_len);
+  if ((long long)B * dims->Hkv * plan.attn.nqblk * plan.attn.nsplit > 2147483647LL)
+    return TV_ENOTSUP;
+  if (!workspace || ws_bytes < plan.ws_bytes) return TV_EWORKSPACE;
+  return hip_status(tv::launch_verify_pass(*dims, *weights, plan, tokens, parent, seq_lens,
+                                           k_cache, v_cache, B, N, Lcap, max_seq_len, argmax,
+                                           logits, hidden_out, workspace, dev_status,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t tv_kv_compact_layers_workspace(int B) {
+  return B < 1 ? 0 : ((size_t)B * 4 + 255) / 256 * 256;
+}
+
+int tv_kv_compact_layers(void* k_cache, void* v_cache, int32_t* seq_lens, const int32_t* path,
+                         const int32_t* path_len, int B, int Hkv, int D, int Lcap, int P,
+                         int layers, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+  if (!k_cache || !v_cache || !seq_lens || !path || !path_len) return TV_EINVAL;
+  if (B < 1 || Hkv < 1 || D < 1 || Lcap < 1 || P < 1 || layers < 1) return TV_EINVAL;
+  if (!dtype_ok(dtype)) return TV_ENOTSUP;
+  const int esz = dtype == TV_F32 ? 4 : 2;
+  if ((D * esz) % 16 || P > 64 || (long long)P * D * esz > 65536) return TV_ENOTSUP;
+  if (B > 65535 || (long long)layers * 2 * Hkv > 2147483647LL) return TV_ENOTSUP;
+  if (!workspace || ws_bytes < tv_kv_compact_layers_workspace(B)) return TV_EWORKSPACE;
+  return hip_status(tv::launch_kv_compact_layers(k_cache, v_cache, seq_lens, path, path_len, B,
+                                                 Hkv, D, Lcap, P, layers, dtype,
+                                                 static_cast<unsigned*>(workspace),
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- graphs
+
+struct tv_graph {
+  hipGraphExec_t exec;
+};
+
+int tv_graph_begin(void* stream) {
+  if (!stream) return TV_EINVAL;  // the null stream cannot be captured
+  return hip_status(
+      hipStreamBeginCapture(static_cast<hipStream_t>(stream), hipStreamCaptureModeThreadLocal));
+}
+
+int tv_graph_end(void* stream, tv_graph** graph) {
+  if (!stream || !graph) return TV_EINVAL;
+  *graph = nullptr;
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(static_cast<hipStream_t>(stream), &g);
+  if (e != hipSuccess) return hip_status(e);
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (e != hipSuccess) return hip_status(e);
+  *graph = new tv_graph{exec};
+  return TV_OK;
+}
+
+int tv_graph_launch(const tv_graph* graph, void* stream) {
+  if (!graph) return TV_EINVAL;
+  return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)));
+}
+
+int tv_graph_destroy(tv_graph* graph) {
+  if (!graph) return TV_EINVAL;
+  const hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -12,9 +12,12 @@
 //
 // One workgroup per sequence handles every plane (K and V of every KV head)
 // and then updates that sequence's length itself, so one launch does the
-// whole commit.  In-place hazard: move j reads row L+path[j], which move
-// j' < j may be writing when path[j] == j'; the hazard exists only inside a
-// plane.  The workgroup therefore stages whole planes - all moved rows of a
+// whole commit.  For the caches of every layer of a model ([layers][B][Hkv]
+// [Lcap][row]), the planes of all layers are shared out among several
+// workgroups per sequence; the last to finish updates the length.
+//
+// In-place hazard: move j reads row L+path[j], which move j' < j may be
+// writing when path[j] == j'; the hazard exists only inside a plane.  The workgroup therefore stages whole planes - all moved rows of a
 // group of planes - in LDS, waits at a barrier and only then writes.  Rows
 // with path[j] == j are skipped.  Accesses are 16-byte vectors, consecutive
 // threads on consecutive 16-byte pieces of a row.
@@ -50,16 +53,20 @@ template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void compact_kernel(
     char* __restrict__ kc, char* __restrict__ vc, int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ path, const int32_t* __restrict__ path_len, int Hkv, int Lcap,
-    int P, int row_bytes, PagedArgs pa) {
+    int P, int row_bytes, PagedArgs pa, int layers, long long layer_bytes, int groups,
+    unsigned* __restrict__ counters) {
   __shared__ uint4 stage[kStageBytes / 16];
   __shared__ int16_t s_move[64];  // j of every row that moves
   __shared__ int s_nmove;
-  const int b = blockIdx.x;
+  __shared__ int s_last;
+  const int b = blockIdx.x / groups;
+  const int grp = blockIdx.x - b * groups;
   const int tid = threadIdx.x;
   const int L = seq_lens[b];
   int n = path_len[b];
   n = n < 0 ? 0 : (n > P ? P : n);
-  // caller contract broken: touch nothing (the length is left as it was)
+  // caller contract broken: touch nothing (the length is left as it was);
+  // every workgroup of the sequence takes this branch together
   if (L < 0 || L + n > Lcap) return;
   const int32_t* pth = path + (size_t)b * P;
   if (tid == 0) {
@@ -74,11 +81,20 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
   const int m = s_nmove;
   const int chunks = row_bytes / 16;
   const int per_plane = m * chunks;  // staged pieces per plane
-  const int planes = 2 * Hkv;
+  // planes (layer, K|V, head) of all layers, shared out among the groups
+  const int planes_all = 2 * Hkv * layers;
+  const int pb = (int)((long long)grp * planes_all / groups);
+  const int pe = (int)((long long)(grp + 1) * planes_all / groups);
+  auto plane_base = [&](int p, int& h) -> char* {
+    const int ly = p / (2 * Hkv);
+    const int q = p - ly * 2 * Hkv;
+    h = q < Hkv ? q : q - Hkv;
+    return (q < Hkv ? kc : vc) + (long long)ly * layer_bytes;
+  };
   if (per_plane > 0) {
     const int group = (kStageBytes / 16) / per_plane;  // >= 1: P * row_bytes <= 64 KB
-    for (int p0 = 0; p0 < planes; p0 += group) {
-      const int pn = min(group, planes - p0);
+    for (int p0 = pb; p0 < pe; p0 += group) {
+      const int pn = min(group, pe - p0);
       const int items = pn * per_plane;
       for (int it = tid; it < items; it += kThreads) {
         const int p = p0 + it / per_plane;
@@ -86,10 +102,10 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
         const int k = rem / chunks;
         const int x = rem - k * chunks;
         const int j = s_move[k];
-        const long long off =
-            row_offset<PAGED>(pa, b, p < Hkv ? p : p - Hkv, Hkv, Lcap, L + pth[j], row_bytes);
-        if (off >= 0)
-          stage[it] = reinterpret_cast<const uint4*>((p < Hkv ? kc : vc) + off)[x];
+        int h;
+        const char* base = plane_base(p, h);
+        const long long off = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + pth[j], row_bytes);
+        if (off >= 0) stage[it] = reinterpret_cast<const uint4*>(base + off)[x];
       }
       __syncthreads();
       for (int it = tid; it < items; it += kThreads) {
@@ -98,16 +114,32 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
         const int k = rem / chunks;
         const int x = rem - k * chunks;
         const int j = s_move[k];
-        const int h = p < Hkv ? p : p - Hkv;
+        int h;
+        char* base = plane_base(p, h);
         const long long src = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + pth[j], row_bytes);
         const long long off = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + j, row_bytes);
-        if (off >= 0 && src >= 0)
-          reinterpret_cast<uint4*>((p < Hkv ? kc : vc) + off)[x] = stage[it];
+        if (off >= 0 && src >= 0) reinterpret_cast<uint4*>(base + off)[x] = stage[it];
       }
       __syncthreads();
     }
   }
-  if (tid == 0) seq_lens[b] = L + n;  // every thread read L before the barriers above
+  // The new length: every workgroup of the sequence has read L (before its
+  // barriers above).  With one workgroup it writes directly; otherwise the
+  // last one to arrive at the counter writes it and clears the counter.  The
+  // counter's return value orders the arrivals; no data passes through it.
+  if (groups == 1) {
+    if (tid == 0) seq_lens[b] = L + n;
+    return;
+  }
+  if (tid == 0) {
+    const unsigned prev =
+        __hip_atomic_fetch_add(&counters[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (unsigned)groups - 1u;
+    if (s_last) {
+      seq_lens[b] = L + n;
+      __hip_atomic_store(&counters[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 }  // namespace
@@ -123,12 +155,32 @@ hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t*
     Lcap = max_blocks << pa.page_shift;
     hipLaunchKernelGGL(compact_kernel<true>, dim3(B), dim3(kThreads), 0, stream,
                        static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len,
-                       Hkv, Lcap, P, row_bytes, pa);
+                       Hkv, Lcap, P, row_bytes, pa, 1, 0LL, 1, nullptr);
   } else {
     hipLaunchKernelGGL(compact_kernel<false>, dim3(B), dim3(kThreads), 0, stream,
                        static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len,
-                       Hkv, Lcap, P, row_bytes, pa);
+                       Hkv, Lcap, P, row_bytes, pa, 1, 0LL, 1, nullptr);
   }
+  return hipGetLastError();
+}
+
+// Every layer in one launch: about eight planes per workgroup, at most 1024
+// workgroups in all.
+hipError_t launch_kv_compact_layers(void* k, void* v, int32_t* seq_lens, const int32_t* path,
+                                    const int32_t* path_len, int B, int Hkv, int D, int Lcap,
+                                    int P, int layers, int dtype, unsigned* counters,
+                                    hipStream_t stream) {
+  const int row_bytes = D * (dtype == TV_F32 ? 4 : 2);
+  const long long layer_bytes = (long long)B * Hkv * Lcap * row_bytes;
+  const int planes = 2 * Hkv * layers;
+  int groups = (planes + 7) / 8;
+  const int cap = 1024 / B > 1 ? 1024 / B : 1;
+  if (groups > cap) groups = cap;
+  if (groups < 1) groups = 1;
+  PagedArgs pa{nullptr, 0, 0, 0};
+  hipLaunchKernelGGL(compact_kernel<false>, dim3(B * groups), dim3(kThreads), 0, stream,
+                     static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len, Hkv,
+                     Lcap, P, row_bytes, pa, layers, layer_bytes, groups, counters);
   return hipGetLastError();
 }
 

@@ -85,12 +85,29 @@ __device__ __forceinline__ size_t packed_offset(int vt, int c, int nk, int j, in
   return (((((size_t)vt * nk + c) * 8 + j) * 4 + s) * 64 + lane) * 8;
 }
 
-template <bool PACKED, int MB, bool PARTIAL>
+// What a workgroup does with its tile of products.
+enum : int {
+  kArgmaxCommit = 0,   // fold per-row keys into the global keys (M <= 64)
+  kArgmaxPartial = 1,  // write one key per (row, vocabulary tile)
+  kStorePartial = 2,   // write the fp32 partial sums of its k range (projections)
+};
+
+// MODE kStorePartial computes out = H W^T for a linear layer (V = output
+// features): workgroup (mt, vt, ks) covers k chunks [cb, ce) of the split ks
+// of nsplit and writes its partial sums to part[ks][M][V]; an epilogue
+// kernel adds the splits in a fixed order, so the result is deterministic.
+//
+// RING is the depth of the register ring of W chunks (loads in flight per
+// wavefront): 2 where several workgroups share a CU (the LM head), 4 for the
+// projections, which run about one workgroup per CU and need the deeper
+// pipeline to keep enough bytes in flight.
+template <bool PACKED, int MB, int MODE, int RING = 2>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MB == 4 ? 2 : 1)))
 void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
                         int32_t* __restrict__ argmax, float* __restrict__ logits,
                         unsigned long long* __restrict__ keys, unsigned* __restrict__ counter,
-                        int M, int K, int V, int nmt, int total_blocks) {
+                        int M, int K, int V, int nmt, int total_blocks, float* __restrict__ part,
+                        int nsplit) {
   constexpr int kRowsM = 16 * MB;                  // hidden-state rows per workgroup
   constexpr int HP = kRowsM * (kKC / 8) / kThreads;  // 16-byte H pieces per thread per stage
   __shared__ __attribute__((aligned(16))) bf16_t sH[2][kRowsM * kHRow];
@@ -105,10 +122,16 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 
   const int lid = xcd_remap(blockIdx.x, total_blocks);
   const int mt = lid % nmt;
-  const int vt = lid / nmt;
+  const int vs = lid / nmt;
+  const int ks = vs % nsplit;
+  const int vt = vs / nsplit;
   const int m0 = mt * kRowsM;
   const int v0 = vt * kVT;
   const int nk = K / kKC;
+  // this split's k chunks [cb, cb + nkl): whole groups of RING chunks
+  const int ngroup = nk / RING;
+  const int cb = RING * (ks * ngroup / nsplit);
+  const int nkl = RING * ((ks + 1) * ngroup / nsplit) - cb;
 
   // W source of this lane (clamped rows in the row-major layout; the packed
   // layout is zero-padded to whole tiles)
@@ -118,20 +141,19 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
     const int v = v0 + wave * 32 + vb * 16 + l16;
     wrow[vb] = W + (size_t)(v < V ? v : V - 1) * K + 32 * kg;
   }
-  auto wload = [&](int c, int vb, int s) -> uint4 {
+  auto wload = [&](int c, int vb, int s) -> u32x4_t {
     if constexpr (PACKED && MB == 4) {
       // one row block (M <= 64): every W byte is read once, so the loads are
       // non-temporal (measured 6% faster on the packed layout, slower on the
       // row-major one)
-      const u32x4_t t = __builtin_nontemporal_load(
+      return __builtin_nontemporal_load(
           reinterpret_cast<const u32x4_t*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane)));
-      return make_uint4(t.x, t.y, t.z, t.w);
     } else if constexpr (PACKED) {
       // several row blocks share each W tile (neighbouring workgroups on one
       // XCD): keep it cacheable so the re-reads hit L2
-      return *reinterpret_cast<const uint4*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane));
+      return *reinterpret_cast<const u32x4_t*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane));
     } else {
-      return *reinterpret_cast<const uint4*>(wrow[vb] + c * kKC + 8 * s);
+      return *reinterpret_cast<const u32x4_t*>(wrow[vb] + c * kKC + 8 * s);
     }
   };
   // this thread's 16-byte pieces of each hidden-state stage (clamped rows)
@@ -146,16 +168,16 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
     hdst[i] = r * kHRow + x * 8;
   }
 
-  uint4 wb[2][2][4];  // [ring slot][16-row block][piece]
+  u32x4_t wb[RING][2][4];  // [ring slot][16-row block][piece]
   uint4 hreg[HP];
 #pragma unroll
-  for (int d = 0; d < 2; ++d)
+  for (int d = 0; d < RING; ++d)
 #pragma unroll
     for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) wb[d][vb][s] = wload(min(d, nk - 1), vb, s);
+      for (int s = 0; s < 4; ++s) wb[d][vb][s] = wload(cb + min(d, nkl - 1), vb, s);
 #pragma unroll
-  for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i]);
+  for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i] + cb * kKC);
 #pragma unroll
   for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(&sH[0][hdst[i]]) = hreg[i];
   __syncthreads();
@@ -166,16 +188,17 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // nk is even (K is a multiple of 256): two chunks per trip keep the ring
-  // slot and the LDS buffer compile-time constants.
-  for (int c0 = 0; c0 < nk; c0 += 2) {
+  // nkl is a multiple of RING (K is a multiple of 256, splits take whole
+  // groups): RING chunks per trip keep the ring slot and the LDS buffer
+  // compile-time constants.
+  for (int c0 = 0; c0 < nkl; c0 += RING) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < RING; ++u) {
       const int c = c0 + u;
-      const int ch = min(c + 1, nk - 1);
+      const int ch = cb + min(c + 1, nkl - 1);
 #pragma unroll
       for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i] + ch * kKC);
-      const bf16_t* sh = sH[u];
+      const bf16_t* sh = sH[u & 1];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -185,24 +208,44 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 #pragma unroll
           for (int vb = 0; vb < 2; ++vb) {
             Frag8 wf;
-            wf.u = wb[u][vb][s];
+            wf.q = wb[u][vb][s];
             acc[vb][mb] = mfma16x16x32(wf.v, hf.v, acc[vb][mb]);
           }
         }
       }
-      const int cw = min(c + 2, nk - 1);
+      const int cw = cb + min(c + RING, nkl - 1);
 #pragma unroll
       for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) wb[u][vb][s] = wload(cw, vb, s);
 #pragma unroll
-      for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(&sH[u ^ 1][hdst[i]]) = hreg[i];
+      for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(&sH[(u & 1) ^ 1][hdst[i]]) = hreg[i];
       __syncthreads();
     }
   }
 
   // ---- epilogue: lane holds rows v = v0 + wave*32 + vb*16 + 4*kg + r of
   // hidden-state row m = m0 + mb*16 + l16
+  if constexpr (MODE == kStorePartial) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m0 + mb * 16 + l16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) {
+        const int vbase = v0 + wave * 32 + vb * 16 + 4 * kg;
+        float* dst = part + ((size_t)ks * M + m) * V + vbase;
+        if ((V & 3) == 0 && vbase + 3 < V) {
+          *reinterpret_cast<f32x4_t*>(dst) = acc[vb][mb];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (vbase + r < V) dst[r] = acc[vb][mb][r];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + mb * 16 + l16;
@@ -243,7 +286,7 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
     s_rowkey[tid] = k;
   }
   __syncthreads();
-  if constexpr (PARTIAL) {
+  if constexpr (MODE == kArgmaxPartial) {
     // one key per (row, vocabulary tile); argmax_reduce_kernel finishes
     const int nvt = total_blocks / nmt;
     if (tid < kRowsM && m0 + tid < M) keys[(size_t)(m0 + tid) * nvt + vt] = s_rowkey[tid];
@@ -411,19 +454,61 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
   const dim3 grid(total), block(kThreads);
   if (mb != 4)
     keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lmhead_zero_bytes(M));
-#define TV_LM_LAUNCH(P, MBV, PART)                                                          \
-  hipLaunchKernelGGL((lmhead_bf16_kernel<P, MBV, PART>), grid, block, 0, stream, h, wv, argmax, \
-                     logits, keys, counter, M, K, V, nmt, total)
+#define TV_LM_LAUNCH(P, MBV, MODEV)                                                         \
+  hipLaunchKernelGGL((lmhead_bf16_kernel<P, MBV, MODEV>), grid, block, 0, stream, h, wv, argmax, \
+                     logits, keys, counter, M, K, V, nmt, total, nullptr, 1)
   if (mb == 4) {
-    if (pk) TV_LM_LAUNCH(true, 4, false); else TV_LM_LAUNCH(false, 4, false);
+    if (pk) TV_LM_LAUNCH(true, 4, kArgmaxCommit); else TV_LM_LAUNCH(false, 4, kArgmaxCommit);
   } else {
-    if (pk) TV_LM_LAUNCH(true, 8, true); else TV_LM_LAUNCH(false, 8, true);
+    if (pk) TV_LM_LAUNCH(true, 8, kArgmaxPartial); else TV_LM_LAUNCH(false, 8, kArgmaxPartial);
   }
 #undef TV_LM_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || mb == 4) return e;
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, keys, argmax,
                      M, nvt);
+  return hipGetLastError();
+}
+
+// Ring depth of the projection kernel: 4 for one row block when K holds whole
+// groups of four chunks, else 2.
+static int proj_ring(int M, int K) {
+  return lmhead_mb(M) == 4 && (K / kKC) % 4 == 0 ? 4 : 2;
+}
+
+// Splits of a projection: the largest count that divides the k groups evenly
+// and keeps the grid at one workgroup per CU or fewer (a partly doubled-up
+// grid runs at the speed of its doubled CUs: measured 40% slower at 320
+// workgroups than at 256 for the 4096 x 4096 case).
+int proj_splits(int M, int K, int Nout) {
+  const int nmt = (M + 16 * lmhead_mb(M) - 1) / (16 * lmhead_mb(M));
+  const int tiles = nmt * ((Nout + kVT - 1) / kVT);
+  const int ngroup = K / (kKC * proj_ring(M, K));
+  int best = 1;
+  for (int s = 1; s <= ngroup; ++s)
+    if (ngroup % s == 0 && (long)s * tiles <= 256) best = s;
+  return best;
+}
+
+hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, int M, int K,
+                       int Nout, int nsplit, hipStream_t stream) {
+  const int mb = lmhead_mb(M);
+  const int nmt = (M + 16 * mb - 1) / (16 * mb);
+  const int total = nmt * ((Nout + kVT - 1) / kVT) * nsplit;
+  const bf16_t* h = static_cast<const bf16_t*>(hidden);
+  const bf16_t* wv = static_cast<const bf16_t*>(w_packed);
+  if (mb == 4 && proj_ring(M, K) == 4)
+    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 4>), dim3(total),
+                       dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
+                       K, Nout, nmt, total, part, nsplit);
+  else if (mb == 4)
+    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 2>), dim3(total),
+                       dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
+                       K, Nout, nmt, total, part, nsplit);
+  else
+    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 8, kStorePartial, 2>), dim3(total),
+                       dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
+                       K, Nout, nmt, total, part, nsplit);
   return hipGetLastError();
 }
 

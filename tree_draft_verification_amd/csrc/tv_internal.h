@@ -37,6 +37,7 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 union Frag8 {  // eight bf16 values as one MFMA operand or one 16-byte load
   uint4 u;
+  u32x4_t q;
   bf16x8_t v;
 };
 
@@ -119,5 +120,38 @@ hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t*
                              int Lcap, int P, int dtype, hipStream_t stream,
                              const int32_t* block_table = nullptr, int max_blocks = 0,
                              int page_size = 0, int num_pages = 0);
+
+// ---------------------------------------------------------------- projections
+
+// Split count of a packed-weight projection out[M][Nout] = H[M][K] W^T.
+int proj_splits(int M, int K, int Nout);
+
+// fp32 partial sums part[nsplit][M][Nout] (W packed as by launch_lmhead_pack).
+hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, int M, int K,
+                       int Nout, int nsplit, hipStream_t stream);
+
+// ---------------------------------------------------------------- multi-layer pass
+
+struct PassPlan {
+  int s_qkv, s_o, s_gu, s_down;  // split-K factors of the four projections
+  AttnPlan attn;
+  size_t off_lm, off_pos, off_x, off_gin, off_q, off_part, off_attn;  // workspace offsets
+  size_t ws_bytes;
+};
+
+PassPlan pass_plan(const tv_model_dims& d, int B, int N, int max_seq_len);
+size_t packed_layer_bytes(int rows, int K);
+
+hipError_t launch_verify_pass(const tv_model_dims& d, const tv_model_weights& w,
+                              const PassPlan& p, const int32_t* tokens, const int32_t* parent,
+                              const int32_t* seq_lens, void* k_cache, void* v_cache, int B,
+                              int N, int Lcap, int max_seq_len, int32_t* argmax, float* logits,
+                              float* hidden_out, void* ws, int32_t* dev_status,
+                              hipStream_t stream);
+
+hipError_t launch_kv_compact_layers(void* k, void* v, int32_t* seq_lens, const int32_t* path,
+                                    const int32_t* path_len, int B, int Hkv, int D, int Lcap,
+                                    int P, int layers, int dtype, unsigned* counters,
+                                    hipStream_t stream);
 
 }  // namespace tv
