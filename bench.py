@@ -10,13 +10,15 @@ LM head, whose per-launch time is taken with HIP events on the launch
 stream), and the fp64 oracle timed on this host's cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--paged PAGE_SIZE] [--model qwen3_8b]
+                    [--paged PAGE_SIZE] [--model qwen3_8b] [--tree CONFIG]
 
 --paged keeps the key/value caches in pages of a shared pool (placed by a
 seeded random permutation) and runs the paged attention and compaction calls.
 --model runs the whole multi-layer verification step instead (36 Qwen3-8B-
 shaped layers with synthetic weights, LM head, acceptance, one compaction
 launch for every layer), captured once as a graph and replayed.
+--tree times draft-tree construction (tv_tree_build) on a named configuration
+of draft-head log-probabilities (e.g. quickstart_d20_w7_n128).
 """
 from __future__ import annotations
 
@@ -135,6 +137,8 @@ def main():
                     help="page size of a paged key/value cache (0: contiguous caches)")
     ap.add_argument("--model", default=None,
                     help="time the multi-layer pass of this synthetic model (e.g. qwen3_8b)")
+    ap.add_argument("--tree", default=None,
+                    help="time draft-tree construction on this configuration")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many bytes")
     args = ap.parse_args()
@@ -147,6 +151,9 @@ def main():
         return
     if args.model:
         model_bench(args)
+        return
+    if args.tree:
+        tree_bench(args)
         return
 
     import torch
@@ -476,6 +483,73 @@ def model_bench(args):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = model_cpu_baseline(cfg, wl, w)
         progress("cpu baseline timed")
+    print(json.dumps(res), flush=True)
+
+
+def tree_bench(args):
+    import torch
+
+    import tree_draft_verification_amd as tv
+    from workloads import TREE_BUILDS, draft_logp
+
+    cfg = TREE_BUILDS[args.tree]
+    x = draft_logp(cfg)
+    dev = torch.device("cuda:0")
+    lp = torch.from_numpy(x["logp"]).to(dev)
+    root = torch.from_numpy(x["root_tokens"]).to(dev)
+    N = cfg.budget + 1
+    par = torch.empty((cfg.B, N), dtype=torch.int32, device=dev)
+    tok = torch.empty((cfg.B, N), dtype=torch.int32, device=dev)
+    ws = torch.zeros(tv.tv_tree_build_workspace(cfg.B, cfg.depth, cfg.V, cfg.width),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        tv.tv_tree_build(lp, root, cfg.width, cfg.budget, parent=par, tokens=tok, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        tv.tv_tree_build(lp, root, cfg.width, cfg.budget, parent=par, tokens=tok, workspace=ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in ev])
+    us = float(np.median(per))
+    nbytes = cfg.B * cfg.depth * cfg.V * 4 + cfg.B * N * 8
+    achieved = nbytes / (us * 1e-6) / 1e9
+    res = {
+        "metric": "draft trees built/s (tv_tree_build: vocabulary top-k + accum_logp tree)",
+        "value": round(cfg.B * args.steps / (t1 - t0), 1), "unit": "trees/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32 (scores summed in f64)",
+        "data": "synthetic (seeded draft log-probabilities)",
+        "config": {"workload": cfg.name, "batch": cfg.B, "depth": cfg.depth,
+                   "width": cfg.width, "budget": cfg.budget, "vocab": cfg.V},
+        "step_us": round(us, 2),
+        "step_us_p10_p90": [round(float(np.percentile(per, 10)), 2),
+                            round(float(np.percentile(per, 90)), 2)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole call (top-k pass + tree kernel)",
+                     "algorithmic_bytes": nbytes, "launch_us": round(us, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while reps < 20 and (reps == 0 or time.perf_counter() - t0 < 20.0):
+            oracle.accum_logp_tree(x["logp"], x["root_tokens"], cfg.width, cfg.budget)
+            reps += 1
+        spent = time.perf_counter() - t0
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            cores = 1
+        res["cpu_baseline"] = dict(value=round(cfg.B * reps / spent, 3), unit="trees/s",
+                                   cores=int(cores), kind="oracle",
+                                   sample=f"{reps} full build(s) of {cfg.name} ({spent:.1f} s)")
     print(json.dumps(res), flush=True)
 
 

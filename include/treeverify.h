@@ -327,6 +327,39 @@ int tv_graph_end(void* stream, tv_graph** graph);
 int tv_graph_launch(const tv_graph* graph, void* stream);
 int tv_graph_destroy(tv_graph* graph);
 
+/*
+ * Draft-tree construction by cumulative log-probability: the accum_logp
+ * algorithm of the JetSpec README ("Evaluation": breadth-first
+ * cumulative-log-probability tree, the default), shaped by depth, width and
+ * budget as in its "Quick Start".  Reading of the steps:
+ *   - candidates of depth d (1..depth): the `width` largest entries of
+ *     draft_logp[b][d-1][:], ties to the smaller token id;
+ *   - breadth first from the root (score 0): each node of the level-(d-1)
+ *     frontier gets one child per candidate of depth d, score = parent score
+ *     + logp (summed in fp64), generated in (frontier rank, token rank)
+ *     order; the level-d frontier is the `width` best children (score
+ *     descending, then generation order); every child is a candidate;
+ *   - the tree: the root plus the `budget` best candidates (score
+ *     descending, then shallower, then generation order), numbered by depth
+ *     and generation, so parent[i] < i.
+ *
+ * draft_logp   [B][depth][V] fp32 normalised log-probabilities of the draft
+ *              head (no NaN)
+ * root_tokens  [B] int32: token of node 0 (the last accepted token)
+ * parent, tokens [B][budget+1] int32 (written): the trees, in the layout the
+ *              verification calls read
+ * node_depth   [B][budget+1] int32 or NULL; score [B][budget+1] fp32 or
+ *              NULL (cumulative log-probability, rounded from fp64)
+ * workspace    tv_tree_build_workspace() bytes (scratch)
+ * Supported: width <= 16, depth <= 64, width + (depth-1)*width^2 <= 4096
+ * candidates, budget + 1 <= TV_MAX_NODES, V >= width, budget <= candidates.
+ */
+size_t tv_tree_build_workspace(int B, int depth, int V, int width);
+int tv_tree_build(const float* draft_logp, const int32_t* root_tokens, int B,
+                  int depth, int V, int width, int budget, int32_t* parent,
+                  int32_t* tokens, int32_t* node_depth, float* score,
+                  void* workspace, size_t ws_bytes, void* stream);
+
 /* Text of a status code (TV_EHIP: the HIP error text of the failed launch). */
 const char* tv_status_string(int status);
 

@@ -29,6 +29,7 @@ from .verify import (  # noqa: F401
     tree_attention_paged,
     verify_step,
 )
+from .tree_build import accum_logp_tree, topk_tokens  # noqa: F401
 from .model import (  # noqa: F401
     kv_compact_layers,
     node_positions,

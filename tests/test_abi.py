@@ -43,8 +43,8 @@ def test_header_declares_the_four_calls():
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
               "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
-              "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_status_string",
-              "tv_abi_version"):
+              "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_tree_build",
+              "tv_tree_build_workspace", "tv_status_string", "tv_abi_version"):
         assert n in names
 
 
@@ -219,6 +219,27 @@ def test_pass_host_validation(lib):
     assert lib.tv_graph_end(None, None) == -1
     assert lib.tv_graph_launch(None, None) == -1
     assert lib.tv_graph_destroy(None) == -1
+
+
+def test_tree_build_host_validation(lib):
+    f = lib.tv_tree_build
+    ws = lib.tv_tree_build_workspace(1, 20, 151936, 7)
+    assert ws > 0
+    ok = dict(lp=FAKE, root=FAKE, B=1, D=20, V=151936, W=7, n=128, par=FAKE, tok=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["lp"], a["root"], a["B"], a["D"], a["V"], a["W"], a["n"], a["par"], a["tok"],
+                 None, None, FAKE if "ws" not in kw else kw["ws"], ws, None)
+    assert call(lp=None) == -1
+    assert call(tok=None) == -1
+    assert call(V=5) == -1                       # V < width
+    assert call(W=17) == -2                      # width limit
+    assert call(D=65) == -2                      # depth limit
+    assert call(n=1024) == -2                    # budget + 1 > TV_MAX_NODES
+    assert call(W=16, D=17) == -2                # 16 + 16 * 256 > 4096 candidates
+    assert call(W=2, D=2, n=7) == -1             # budget above the 6 candidates
+    assert call(ws=None) == -3
 
 
 def test_binding_names_match_the_c_calls():

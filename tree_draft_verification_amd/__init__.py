@@ -44,7 +44,8 @@ __all__ = [
     "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace", "tv_kv_compact_paged",
     "Model", "tv_model_pack", "tv_verify_pass", "tv_verify_pass_workspace",
     "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "Graph", "tv_graph_begin",
-    "tv_graph_end", "tv_graph_launch", "tv_graph_destroy",
+    "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_tree_build",
+    "tv_tree_build_workspace",
 ]
 
 
@@ -484,3 +485,41 @@ def tv_graph_destroy(graph: Graph) -> None:
     h, graph.handle = graph.handle, None
     if h:
         _check("tv_graph_destroy", _lib_handle().tv_graph_destroy(h))
+
+
+# ---------------------------------------------------------------- tree construction
+
+def tv_tree_build_workspace(B: int, depth: int, V: int, width: int) -> int:
+    return int(_lib_handle().tv_tree_build_workspace(B, depth, V, width))
+
+
+def tv_tree_build(draft_logp, root_tokens, width: int, budget: int, *, parent=None, tokens=None,
+                  node_depth=None, score=None, workspace=None):
+    """Draft trees by cumulative log-probability.  draft_logp [B,depth,V] fp32;
+    root_tokens [B] int32.  Returns (parent, tokens) [B, budget+1] int32
+    (node_depth / score are filled when given)."""
+    B, D, V = draft_logp.shape
+    if draft_logp.dtype != torch.float32:
+        raise TypeError("draft_logp must be float32")
+    _i32(root_tokens, (B,), "root_tokens")
+    N = budget + 1
+    dev = draft_logp.device
+    if parent is None:
+        parent = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _i32(parent, (B, N), "parent")
+    _i32(tokens, (B, N), "tokens")
+    if node_depth is not None:
+        _i32(node_depth, (B, N), "node_depth")
+    if score is not None and (score.dtype != torch.float32 or tuple(score.shape) != (B, N)):
+        raise ValueError("score must be float32 of shape (B, budget+1)")
+    need = tv_tree_build_workspace(B, D, V, width)
+    if workspace is None:
+        workspace = _cached_workspace("tree_build", need, dev)
+    st = _lib_handle().tv_tree_build(
+        _ptr(draft_logp), _ptr(root_tokens), B, D, V, width, budget, _ptr(parent), _ptr(tokens),
+        _ptr(node_depth), _ptr(score), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("tv_tree_build", st)
+    return parent, tokens

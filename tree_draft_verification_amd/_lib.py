@@ -53,6 +53,8 @@ SIGNATURES = {
                             _p, _p]),
     "tv_kv_compact_layers_workspace": (_sz, [_i]),
     "tv_kv_compact_layers": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p]),
+    "tv_tree_build_workspace": (_sz, [_i, _i, _i, _i]),
+    "tv_tree_build": (_i, [_p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _sz, _p]),
     "tv_graph_begin": (_i, [_p]),
     "tv_graph_end": (_i, [_p, ctypes.POINTER(_p)]),
     "tv_graph_launch": (_i, [_p, _p]),

@@ -304,3 +304,29 @@ int tv_graph_destroy(tv_graph* graph) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- tree construction
+
+extern "C" {
+
+size_t tv_tree_build_workspace(int B, int depth, int V, int width) {
+  if (B < 1 || depth < 1 || V < 1 || width < 1) return 0;
+  return tv::tree_build_ws_bytes(B, depth, V, width);
+}
+
+int tv_tree_build(const float* draft_logp, const int32_t* root_tokens, int B, int depth, int V,
+                  int width, int budget, int32_t* parent, int32_t* tokens, int32_t* node_depth,
+                  float* score, void* workspace, size_t ws_bytes, void* stream) {
+  if (!draft_logp || !root_tokens || !parent || !tokens) return TV_EINVAL;
+  if (B < 1 || depth < 1 || V < 1 || width < 1 || budget < 1 || V < width) return TV_EINVAL;
+  if (width > 16 || depth > 64 || budget + 1 > TV_MAX_NODES || B > 65535) return TV_ENOTSUP;
+  if ((long long)width + (long long)(depth - 1) * width * width > 4096) return TV_ENOTSUP;
+  if (budget > tv::tree_build_pool(depth, width)) return TV_EINVAL;
+  if ((long long)B * depth * V > (1LL << 40)) return TV_ENOTSUP;
+  if (!workspace || ws_bytes < tv::tree_build_ws_bytes(B, depth, V, width)) return TV_EWORKSPACE;
+  return hip_status(tv::launch_tree_build(draft_logp, root_tokens, B, depth, V, width, budget,
+                                          parent, tokens, node_depth, score, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,362 @@
+// Draft-tree construction by cumulative log-probability (accum_logp).
+//
+// The JetSpec README ("Evaluation") names accum_logp, a breadth-first
+// cumulative-log-probability tree, as the default tree algorithm; its "Quick
+// Start" shapes the tree by a depth, a width and a node budget.  From the
+// draft head's normalised log-probabilities logp[b][d][V] (one row per depth):
+//   * the candidate tokens of depth d are the `width` largest entries of row
+//     d (ties to the smaller id);
+//   * breadth first, every node of the level-(d-1) frontier gets one child
+//     per candidate token, score = parent score + logp; the level-d frontier
+//     is the `width` best children (score, then generation order); every
+//     child is a candidate;
+//   * the tree is the root plus the `budget` best candidates (score, then
+//     depth, then generation), numbered by depth and generation.
+// Scores are fp32 inputs summed in fp64, which is exact here, so every
+// decision is exact.
+//
+// Top lists are kept per wavefront: lanes 0..W-1 hold the wavefront's best
+// keys in order.  An element costs one compare against the wavefront's W-th
+// key and a ballot; only the rare elements that beat it are inserted, all
+// lanes shifting their entry in one step.
+// Kernel 1 (data parallel, HBM bound): one workgroup per (row, vocabulary
+// chunk) writes the chunk's sorted top-W packed (value, id) keys.
+// Kernel 2 (one workgroup of 16 wavefronts per sequence, LDS resident):
+// merges the chunk lists of every depth, runs the breadth-first levels in
+// one wavefront, keeps the budget's best candidates (bitonic sort) and
+// numbers the kept nodes by a scan.
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+constexpr int kTopThreads = 256;    // kernel 1
+constexpr int kTreeThreads = 1024;  // kernel 2
+constexpr int kMaxW = 16;           // width limit (wavefront list)
+constexpr int kMaxPool = 4096;      // candidate pool limit
+constexpr int kMaxDepth = 64;
+
+typedef unsigned long long u64;
+
+__device__ __forceinline__ u64 shfl_up1_u64(u64 x) {
+  const uint32_t lo = __shfl_up((uint32_t)x, 1, 64);
+  const uint32_t hi = __shfl_up((uint32_t)(x >> 32), 1, 64);
+  return ((u64)hi << 32) | lo;
+}
+
+__device__ __forceinline__ u64 readlane_u64(u64 x, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+  return ((u64)hi << 32) | lo;
+}
+
+// Order-preserving map of fp64 to u64 (larger value -> larger key; any
+// non-NaN value maps above 0, the empty-slot key).
+__device__ __forceinline__ u64 f64_order_key(double d) {
+  const u64 u = (u64)__double_as_longlong(d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Inverse of f32_order_key on the high half of an argmax key.
+__device__ __forceinline__ float key_value(u64 k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+__device__ __forceinline__ int key_token(u64 k) { return (int)(~(uint32_t)(k & 0xffffffffull)); }
+
+// A wavefront's sorted list: lane i < W holds its i-th best key L (0 when
+// empty) and a payload P.  offer() inserts every lane's key k that beats the
+// W-th entry, in lane order; an equal key never passes an entry already in
+// the list, so among equal keys the earlier offered ranks first.
+struct WaveList {
+  u64 L = 0ull;
+  int P = 0;
+  u64 thr = 0ull;  // W-th key (wave uniform)
+
+  __device__ __forceinline__ void offer(u64 k, int payload, int W, int lane) {
+    u64 m = __ballot(k > thr);
+    while (m) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const u64 kk = readlane_u64(k, src);
+      if (kk <= thr) continue;  // the threshold rose since the ballot
+      const int pp = __builtin_amdgcn_readlane(payload, src);
+      const u64 up = shfl_up1_u64(L);
+      const int upp = __shfl_up(P, 1, 64);
+      if (lane < W && L < kk) {
+        const bool here = lane == 0 || up >= kk;
+        L = here ? kk : up;
+        P = here ? pp : upp;
+      }
+      thr = readlane_u64(L, W - 1);
+    }
+  }
+};
+
+// Rank of (v, i) among a[0..n) in LDS: entries greater than v, or equal to
+// it at a smaller index.  Eight independent reads per trip (the count is
+// bound by LDS latency otherwise; more would exceed the register budget of
+// a 1024-thread workgroup).
+template <typename T>
+__device__ __forceinline__ int rank_among(const T* a, int n, T v, int i) {
+  int r = 0, j = 0;
+  for (; j + 8 <= n; j += 8) {
+    T x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = a[j + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r += (x[u] > v) | ((x[u] == v) & (j + u < i));
+  }
+  for (; j < n; ++j) r += (a[j] > v) | ((a[j] == v) & (j < i));
+  return r;
+}
+
+// ---- kernel 1: sorted top-W keys of one vocabulary chunk of one row.
+__global__ __launch_bounds__(kTopThreads) void draft_topk_kernel(
+    const float* __restrict__ logp, int V, int W, int nch, int chunk_len, u64* __restrict__ part) {
+  __shared__ u64 s_wl[kTopThreads / 64][kMaxW];
+  const int row = blockIdx.x / nch;
+  const int c = blockIdx.x - row * nch;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int v0 = c * chunk_len;
+  const int v1 = min(V, v0 + chunk_len);
+  const float* x = logp + (size_t)row * V;
+  WaveList wl;
+  // eight independent loads per trip (clamped addresses), then the offers;
+  // the trip count is uniform across the wavefront (offer() uses ballots)
+  constexpr int kBatch = 8;
+  for (int b0 = v0 + wave * 64; b0 < v1; b0 += kBatch * kTopThreads) {
+    float val[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) val[u] = x[min(b0 + u * kTopThreads + lane, v1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int v = b0 + u * kTopThreads + lane;
+      // + 0.0f turns -0.0 into +0.0, so equal values tie on the token id
+      const u64 k = v < v1 ? argmax_key(val[u] + 0.0f, (uint32_t)v) : 0ull;
+      wl.offer(k, 0, W, lane);
+    }
+  }
+  if (lane < W) s_wl[wave][lane] = wl.L;
+  __syncthreads();
+  if (wave == 0) {  // merge the four lists (keys are unique)
+    const int n = (kTopThreads / 64) * W;
+    WaveList m;
+    const u64 k = lane < n ? s_wl[lane / W][lane % W] : 0ull;
+    m.offer(k, 0, W, lane);
+    if (lane < W) part[(size_t)blockIdx.x * kMaxW + lane] = m.L;
+  }
+}
+
+// ---- kernel 2: the tree of one sequence.
+__global__ __launch_bounds__(kTreeThreads) void tree_build_kernel(
+    const u64* __restrict__ part, const int32_t* __restrict__ root_tokens, int D, int W,
+    int nch, int budget, int32_t* __restrict__ parent_out, int32_t* __restrict__ token_out,
+    int32_t* __restrict__ depth_out, float* __restrict__ score_out) {
+  __shared__ double s_score[kMaxPool];       // chunk lists, then pool scores, then sort keys
+  __shared__ int16_t s_id[kMaxPool];         // sort payload: pool index
+  __shared__ int16_t s_par[kMaxPool];        // parent pool index (-1: root)
+  __shared__ int32_t s_tok[kMaxPool];
+  __shared__ int8_t s_dep[kMaxPool];
+  __shared__ int16_t s_node[kMaxPool];       // node number of a kept entry, else -1
+  __shared__ float s_kscore[kMaxPool];       // fp32 score of a kept entry
+  __shared__ int32_t s_ctok[kMaxDepth][kMaxW];
+  __shared__ float s_clp[kMaxDepth][kMaxW];
+  __shared__ int s_fidx[kMaxW];
+  __shared__ double s_fscore[kMaxW];
+  __shared__ int s_wsum[kTreeThreads / 64];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  constexpr int kWaves = kTreeThreads / 64;
+
+  // A. candidates of every depth: the chunks' sorted lists are staged in LDS
+  // (D * nch * W <= kMaxPool) and merged into a wavefront list, one
+  // wavefront per depth (keys are unique)
+  u64* s_lists = reinterpret_cast<u64*>(s_score);
+  for (int e = tid; e < D * nch * W; e += kTreeThreads) {
+    const int r = e % W, dc = e / W;  // dc = d * nch + c
+    s_lists[e] = part[((size_t)b * D * nch + dc) * kMaxW + r];
+  }
+  __syncthreads();
+  const int nl = nch * W;
+  for (int d = wave; d < D; d += kWaves) {
+    const u64* lists = s_lists + (size_t)d * nl;
+    WaveList m;
+    for (int i0 = 0; i0 < nl; i0 += 64)
+      m.offer(i0 + lane < nl ? lists[i0 + lane] : 0ull, 0, W, lane);
+    if (lane < W) {
+      s_ctok[d][lane] = key_token(m.L);
+      s_clp[d][lane] = key_value(m.L);
+    }
+  }
+  __syncthreads();  // s_score is free again
+
+  // B. breadth-first levels, all in wavefront 0 (LDS accesses of one
+  // wavefront are ordered, so no barrier is needed between levels): the
+  // children of the frontier in generation order, then the next frontier
+  // by rank counting (score descending, then generation)
+  if (wave == 0) {
+    if (lane == 0) {
+      s_fidx[0] = -1;
+      s_fscore[0] = 0.0;
+    }
+    int base = 0, fsize = 1;
+    for (int d = 1; d <= D; ++d) {
+      const int lsz = fsize * W;
+      for (int t = lane; t < lsz; t += 64) {
+        const int r = t / W, j = t - (t / W) * W;
+        s_score[base + t] = s_fscore[r] + (double)s_clp[d - 1][j];
+        s_par[base + t] = (int16_t)s_fidx[r];
+        s_tok[base + t] = s_ctok[d - 1][j];
+        s_dep[base + t] = (int8_t)d;
+      }
+      int nidx[4];
+      double nsc[4];
+      int nrank[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {  // lsz <= 256: up to four children per lane
+        const int t = lane + 64 * q;
+        nrank[q] = kMaxW;
+        if (t < lsz) {
+          const double sc = s_score[base + t];
+          nrank[q] = rank_among(s_score + base, lsz, sc, t);
+          nidx[q] = base + t;
+          nsc[q] = sc;
+        }
+      }
+      // every read of the old frontier is done before it is overwritten
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (nrank[q] < W) {
+          s_fidx[nrank[q]] = nidx[q];
+          s_fscore[nrank[q]] = nsc[q];
+        }
+      }
+      fsize = lsz < W ? lsz : W;
+      base += lsz;
+    }
+    if (lane == 0) s_wsum[0] = base;
+  }
+  __syncthreads();
+  const int C = s_wsum[0];
+  __syncthreads();  // s_wsum is reused by the scan
+
+  // C. keep the `budget` best candidates (score descending, then pool
+  // index, i.e. depth and generation): bitonic sort of the pool
+  {
+    int P2 = 1;
+    while (P2 < C) P2 <<= 1;
+    for (int i = tid; i < P2; i += kTreeThreads) {
+      s_id[i] = (int16_t)i;
+      if (i >= C) s_score[i] = -INFINITY;
+    }
+    __syncthreads();
+    for (int k = 2; k <= P2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P2; i += kTreeThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const double si = s_score[i], sl = s_score[l];
+            const int ii = s_id[i], il = s_id[l];
+            const bool l_better = sl > si || (sl == si && il < ii);
+            const bool swap = ((i & k) == 0) ? l_better : !l_better;
+            if (swap) {
+              s_score[i] = sl;
+              s_score[l] = si;
+              s_id[i] = (int16_t)il;
+              s_id[l] = (int16_t)ii;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < C; i += kTreeThreads) s_node[i] = -1;
+    __syncthreads();
+    for (int r = tid; r < budget; r += kTreeThreads) {
+      const int id = s_id[r];
+      s_node[id] = 1;
+      s_kscore[id] = (float)s_score[r];
+    }
+    __syncthreads();
+  }
+
+  // D. number the kept entries in pool order (block scan)
+  const int per = (C + kTreeThreads - 1) / kTreeThreads;
+  const int lo = min(C, tid * per), hi = min(C, lo + per);
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i) cnt += s_node[i] > 0;
+  int incl = cnt;  // inclusive scan within the wavefront
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int before = 1;  // node 0 is the root
+  for (int w = 0; w < wave; ++w) before += s_wsum[w];
+  int next = before + incl - cnt;
+  for (int i = lo; i < hi; ++i)
+    if (s_node[i] > 0) s_node[i] = (int16_t)next++;
+  __syncthreads();
+
+  // E. outputs
+  const int N = budget + 1;
+  int32_t* par = parent_out + (size_t)b * N;
+  int32_t* tok = token_out + (size_t)b * N;
+  if (tid == 0) {
+    par[0] = -1;
+    tok[0] = root_tokens[b];
+    if (depth_out) depth_out[(size_t)b * N] = 0;
+    if (score_out) score_out[(size_t)b * N] = 0.f;
+  }
+  for (int i = tid; i < C; i += kTreeThreads) {
+    const int n = s_node[i];
+    if (n <= 0) continue;
+    const int pi = s_par[i];
+    const int pn = pi < 0 ? 0 : s_node[pi];
+    par[n] = pn < 0 ? 0 : pn;  // the kept set holds every kept node's parent
+    tok[n] = s_tok[i];
+    if (depth_out) depth_out[(size_t)b * N + n] = s_dep[i];
+    if (score_out) score_out[(size_t)b * N + n] = s_kscore[i];
+  }
+}
+
+// Vocabulary chunks per row: about 512 workgroups in all, chunks of at least
+// 4096 entries, and few enough that every depth's lists fit the tree
+// kernel's LDS staging.
+int tb_chunks(int B, int D, int V, int W) {
+  int nch = (512 + B * D - 1) / (B * D);
+  const int max_by_len = V / 4096 > 0 ? V / 4096 : 1;
+  if (nch > max_by_len) nch = max_by_len;
+  if (nch > kMaxPool / (D * W)) nch = kMaxPool / (D * W);
+  return nch < 1 ? 1 : nch;
+}
+
+}  // namespace
+
+int tree_build_pool(int D, int W) { return W + (D - 1) * W * W; }
+
+size_t tree_build_ws_bytes(int B, int D, int V, int W) {
+  return (size_t)B * D * tb_chunks(B, D, V, W) * kMaxW * sizeof(u64);
+}
+
+hipError_t launch_tree_build(const float* logp, const int32_t* root_tokens, int B, int D, int V,
+                             int W, int budget, int32_t* parent, int32_t* tokens,
+                             int32_t* node_depth, float* score, void* ws, hipStream_t stream) {
+  const int nch = tb_chunks(B, D, V, W);
+  const int chunk_len = (V + nch - 1) / nch;
+  u64* part = static_cast<u64*>(ws);
+  hipLaunchKernelGGL(draft_topk_kernel, dim3(B * D * nch), dim3(kTopThreads), 0, stream, logp,
+                     V, W, nch, chunk_len, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree_build_kernel, dim3(B), dim3(kTreeThreads), 0, stream, part,
+                     root_tokens, D, W, nch, budget, parent, tokens, node_depth, score);
+  return hipGetLastError();
+}
+
+}  // namespace tv

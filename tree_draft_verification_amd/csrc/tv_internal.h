@@ -154,4 +154,12 @@ hipError_t launch_kv_compact_layers(void* k, void* v, int32_t* seq_lens, const i
                                     int P, int layers, int dtype, unsigned* counters,
                                     hipStream_t stream);
 
+// ---------------------------------------------------------------- tree construction
+
+int tree_build_pool(int depth, int width);  // candidate nodes of a tree
+size_t tree_build_ws_bytes(int B, int depth, int V, int width);
+hipError_t launch_tree_build(const float* logp, const int32_t* root_tokens, int B, int depth,
+                             int V, int width, int budget, int32_t* parent, int32_t* tokens,
+                             int32_t* node_depth, float* score, void* ws, hipStream_t stream);
+
 }  // namespace tv

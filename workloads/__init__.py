@@ -13,6 +13,9 @@ from .gen import (  # noqa: F401
     draft_tokens,
     lmhead_inputs,
     paged_layout,
+    TREE_BUILDS,
+    TreeBuildConfig,
+    draft_logp,
     bf16_bits_from_f32,
     BF16_QNAN,
 )

@@ -353,3 +353,49 @@ def paged_layout(k_cache, v_cache, page_size: int, seed: int, extra_pages: int =
         pools.append(pool)
     return dict(k_pages=pools[0], v_pages=pools[1], block_table=block_table,
                 page_size=page_size, num_pages=num_pages)
+
+
+# ----------------------------------------------------------------------------
+# draft-head log-probabilities for tree construction
+
+@dataclass(frozen=True)
+class TreeBuildConfig:
+    """Tree construction from the draft head's per-depth log-probabilities
+    (depth, width and budget as in the JetSpec README's "Quick Start" and
+    "Evaluation" commands)."""
+    name: str
+    B: int
+    depth: int
+    width: int
+    budget: int
+    V: int
+    scale: float = 3.0             # std of the synthetic draft logits
+    quantum: float | None = None   # round logits to this step (makes exact ties)
+    seed: int = 0
+
+
+TREE_BUILDS = {
+    "quickstart_d20_w7_n128": TreeBuildConfig("quickstart_d20_w7_n128", B=1, depth=20, width=7,
+                                              budget=128, V=151936, seed=3001),
+    "bench_d20_w7_n256": TreeBuildConfig("bench_d20_w7_n256", B=1, depth=20, width=7,
+                                         budget=256, V=151936, seed=3002),
+    "batch8_d20_w7_n128": TreeBuildConfig("batch8_d20_w7_n128", B=8, depth=20, width=7,
+                                          budget=128, V=151936, seed=3003),
+}
+
+
+def draft_logp(cfg: TreeBuildConfig) -> dict:
+    """logp [B][depth][V] fp32: log-softmax (fp64, then rounded to fp32) of
+    seeded logits ~ N(0, scale^2), optionally rounded to multiples of
+    `quantum` first; root_tokens [B] uniform ids.  These stand for the draft
+    head's output, which lies outside the tree construction."""
+    s = np.random.SeedSequence(cfg.seed).spawn(2)
+    rng = np.random.default_rng(s[0])
+    logits = cfg.scale * rng.standard_normal((cfg.B, cfg.depth, cfg.V))
+    if cfg.quantum:
+        logits = np.round(logits / cfg.quantum) * cfg.quantum
+    m = logits.max(axis=-1, keepdims=True)
+    lse = m + np.log(np.exp(logits - m).sum(axis=-1, keepdims=True))
+    logp = (logits - lse).astype(np.float32)
+    root = np.random.default_rng(s[1]).integers(0, cfg.V, size=cfg.B).astype(np.int32)
+    return dict(logp=logp, root_tokens=root)
