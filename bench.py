@@ -11,6 +11,7 @@ stream), and the fp64 oracle timed on this host's cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--paged PAGE_SIZE] [--model qwen3_8b] [--tree CONFIG]
+                    [--decode STEPS --model qwen3_8b]
 
 --paged keeps the key/value caches in pages of a shared pool (placed by a
 seeded random permutation) and runs the paged attention and compaction calls.
@@ -19,6 +20,9 @@ shaped layers with synthetic weights, LM head, acceptance, one compaction
 launch for every layer), captured once as a graph and replayed.
 --tree times draft-tree construction (tv_tree_build) on a named configuration
 of draft-head log-probabilities (e.g. quickstart_d20_w7_n128).
+--decode runs STEPS steps of ragged speculative decoding with the model
+(tree construction, multi-layer pass, acceptance, compaction per step) and
+reports generated tokens per second of device time.
 """
 from __future__ import annotations
 
@@ -137,6 +141,11 @@ def main():
                     help="page size of a paged key/value cache (0: contiguous caches)")
     ap.add_argument("--model", default=None,
                     help="time the multi-layer pass of this synthetic model (e.g. qwen3_8b)")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="steps of multi-step speculative decoding (with --model)")
+    ap.add_argument("--tree-depth", type=int, default=20)
+    ap.add_argument("--tree-width", type=int, default=7)
+    ap.add_argument("--tree-budget", type=int, default=63)
     ap.add_argument("--tree", default=None,
                     help="time draft-tree construction on this configuration")
     ap.add_argument("--calibrate-copy", type=int, default=0,
@@ -148,6 +157,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         copy_calibration(args.calibrate_copy)
+        return
+    if args.model and args.decode:
+        decode_bench(args)
         return
     if args.model:
         model_bench(args)
@@ -550,6 +562,140 @@ def tree_bench(args):
         res["cpu_baseline"] = dict(value=round(cfg.B * reps / spent, 3), unit="trees/s",
                                    cores=int(cores), kind="oracle",
                                    sample=f"{reps} full build(s) of {cfg.name} ({spent:.1f} s)")
+    print(json.dumps(res), flush=True)
+
+
+def decode_bench(args):
+    """Multi-step ragged speculative decoding at full size.  The simulated
+    drafter knows the target's greedy continuation from the current state
+    (one-token passes on a scratch copy of the caches) and favours it with
+    probability 0.9 at every depth; the drafter and the host bookkeeping
+    between steps are not timed."""
+    import torch
+
+    import tree_draft_verification_amd as tv
+    from workloads import MODELS, WORKLOADS, model_inputs, model_weights
+
+    cfg = MODELS[args.model]
+    wl = WORKLOADS[args.workload]
+    steps, depth, width, budget = args.decode, args.tree_depth, args.tree_width, args.tree_budget
+    N = budget + 1
+    room = N + steps * (depth + 1)
+    dev = torch.device("cuda:0")
+    t_setup = time.perf_counter()
+
+    def progress(msg):
+        print(f"[bench] {time.perf_counter() - t_setup:6.1f} s  {msg}", file=sys.stderr, flush=True)
+
+    w = model_weights(cfg)
+    x = model_inputs(cfg, wl.replace(N=room))
+    progress("synthetic weights and caches drawn")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    model = tv.tv_model_pack(cfg.dims(), {k: bf(v) for k, v in w.items()})
+    del w
+    k0, v0 = bf(x["k_cache"]), bf(x["v_cache"])
+    del x["k_cache"], x["v_cache"]
+    B, V = wl.B, cfg.V
+    L0 = x["seq_lens"].copy()
+    root0 = x["tokens"][:, 0].copy()
+    Lcap = k0.shape[3]
+    progress("weights packed, caches resident")
+
+    k, v = k0.clone(), v0.clone()
+    ks, vs = torch.empty_like(k0), torch.empty_like(v0)   # scratch of the simulated drafter
+    lens = i32(L0)
+    root = i32(root0)
+    P = 32
+    chain = torch.full((B, 1), -1, dtype=torch.int32, device=dev)
+    ref = torch.empty((B, depth), dtype=torch.int32, device=dev)
+    par = torch.empty((B, N), dtype=torch.int32, device=dev)
+    tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    arg = torch.empty(B * N, dtype=torch.int32, device=dev)
+    path = torch.empty((B, P), dtype=torch.int32, device=dev)
+    plen = torch.empty(B, dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    tb_ws = torch.zeros(tv.tv_tree_build_workspace(B, depth, V, width), dtype=torch.uint8,
+                        device=dev)
+    pass_ws = torch.zeros(tv.tv_verify_pass_workspace(model, B, N, Lcap - N), dtype=torch.uint8,
+                          device=dev)
+    ar_ws = torch.zeros(tv.tv_verify_pass_workspace(model, B, 1, Lcap - 1), dtype=torch.uint8,
+                        device=dev)
+    cl_ws = torch.zeros(tv.tv_kv_compact_layers_workspace(B), dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    rng = np.random.default_rng(wl.seed)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    emitted = np.zeros(B, dtype=np.int64)
+    plens = []
+    cur = L0.copy()
+    for s in range(steps):
+        # simulated drafter (untimed): the target's greedy continuation from
+        # the current state, by one-token passes on a scratch copy of the
+        # caches; each depth favours that token with probability 0.9
+        ks.copy_(k)
+        vs.copy_(v)
+        sl = lens.clone()
+        t1 = root.reshape(B, 1).clone()
+        for d in range(depth):
+            a1 = tv.tv_verify_pass(model, t1, chain, sl, ks, vs, max_seq_len=int(cur.max()) + d,
+                                   workspace=ar_ws)
+            ref[:, d] = a1
+            t1 = a1.reshape(B, 1).clone()
+            sl += 1
+        ref_h = ref.cpu().numpy()
+        logits = torch.randn((B, depth, V), generator=gen, device=dev)
+        for b in range(B):
+            for d in range(depth):
+                t_ = int(ref_h[b, d]) if rng.random() < 0.9 else int(rng.integers(V))
+                logits[b, d, t_] += 12.0
+        logp = torch.log_softmax(logits, dim=-1).contiguous()
+        torch.cuda.synchronize()
+        ev[s][0].record()
+        tv.tv_tree_build(logp, root, width, budget, parent=par, tokens=tokens, workspace=tb_ws)
+        ev[s][1].record()
+        tv.tv_verify_pass(model, tokens, par, lens, k, v, arg, max_seq_len=int(cur.max()),
+                          workspace=pass_ws)
+        ev[s][2].record()
+        tv.tv_tree_accept(par, tokens, arg, P, path=path, path_len=plen, bonus=bonus)
+        ev[s][3].record()
+        tv.tv_kv_compact_layers(k, v, lens, path, plen, workspace=cl_ws)
+        ev[s][4].record()
+        root = bonus.clone()
+        plen_h = plen.cpu().numpy()
+        plens.append(plen_h.tolist())
+        emitted += plen_h
+        cur = lens.cpu().numpy()
+        progress(f"step {s}: path lengths {plen_h.tolist()}")
+        if int(cur.max()) + N > Lcap:
+            break
+    torch.cuda.synchronize()
+    done = len(plens)
+    parts = np.array([[ev[s][j].elapsed_time(ev[s][j + 1]) * 1e3 for j in range(4)]
+                      for s in range(done)])
+    dev_s = parts.sum() * 1e-6
+    res = {
+        "metric": "generated tokens/s, multi-step ragged speculative decoding (device time)",
+        "value": round(float(emitted.sum()) / dev_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": done, "warmup": 0, "ms_per_step": round(parts.sum(axis=1).mean() / 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded weights and caches, drafter favouring the greedy continuation)",
+        "config": {"workload": f"{cfg.name} x {wl.name}", "batch": B,
+                   "prefix": [int(t) for t in L0], "tree_depth": depth, "tree_width": width,
+                   "tree_budget": budget, "parallelism": "none (1 GPU)"},
+        "tokens_per_step": round(float(emitted.sum()) / done, 2),
+        "mean_path_len": round(float(np.mean(plens)), 2),
+        "step_us_breakdown": {"tree_build": round(float(parts[:, 0].mean()), 1),
+                              "verify_pass": round(float(parts[:, 1].mean()), 1),
+                              "accept": round(float(parts[:, 2].mean()), 1),
+                              "compact_layers": round(float(parts[:, 3].mean()), 1)},
+        "path_lens": plens,
+    }
     print(json.dumps(res), flush=True)
 
 

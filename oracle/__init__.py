@@ -31,6 +31,7 @@ from .verify import (  # noqa: F401
 )
 from .tree_build import accum_logp_tree, topk_tokens  # noqa: F401
 from .model import (  # noqa: F401
+    ar_decode,
     kv_compact_layers,
     node_positions,
     rms_norm,

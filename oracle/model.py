@@ -122,7 +122,7 @@ def verify_pass(dims: dict, weights: dict, tokens, parent, seq_lens, k_cache, v_
     top1 = np.full(M, -np.inf)
     top2 = np.full(M, -np.inf)
     arg = np.zeros(M, dtype=np.int64)
-    rows = np.arange(M) if logit_rows is None else np.asarray(logit_rows)
+    rows = np.arange(M) if logit_rows is None else np.asarray(logit_rows, dtype=np.int64)
     logits = np.empty((len(rows), V))
     for v0 in range(0, V, v_chunk):
         lg = hf @ decode(lm[v0:v0 + v_chunk], "bf16").T          # [M][chunk]
@@ -149,3 +149,30 @@ def kv_compact_layers(k_cache, v_cache, seq_lens, path, path_len):
     for ly in range(k.shape[0]):
         k[ly], v[ly], lens = kv_compact(k[ly], v[ly], seq_lens, path, path_len)
     return k, v, lens
+
+
+def ar_decode(dims: dict, weights: dict, k_cache, v_cache, seq_lens, root_tokens,
+              n_tokens: int) -> dict:
+    """Independent greedy decoding of every sequence, one token per pass.
+
+    Sequence b starts from its cached prefix (rows 0..L_b-1) and the token
+    root_tokens[b], whose key/value row is not cached yet (node 0 of a
+    verification tree).  Each step runs a one-node pass at the current
+    length, appends that token's rows and emits the argmax.  Returns the
+    emitted tokens [B][n_tokens], the top-2 gap of each choice, and the
+    caches after the last step (fp64).
+    """
+    B = len(seq_lens)
+    toks = np.asarray(root_tokens, dtype=np.int64).reshape(B, 1)
+    lens = np.asarray(seq_lens, dtype=np.int64).copy()
+    kc, vc = k_cache, v_cache
+    out = np.empty((B, n_tokens), dtype=np.int64)
+    gap = np.empty((B, n_tokens))
+    for t in range(n_tokens):
+        r = verify_pass(dims, weights, toks, np.full((B, 1), -1), lens, kc, vc, logit_rows=[])
+        out[:, t] = r["argmax"]
+        gap[:, t] = r["gap"]
+        kc, vc = r["k_cache"], r["v_cache"]
+        lens = lens + 1
+        toks = r["argmax"].reshape(B, 1)
+    return dict(tokens=out, gap=gap, k_cache=kc, v_cache=vc, seq_lens=lens)

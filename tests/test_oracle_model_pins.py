@@ -204,3 +204,26 @@ def test_m7_compaction_then_bonus_token_continues_the_accepted_path():
         ref = _dense_path_logits(CFG, w, x["k_cache"], x["v_cache"], b, int(x["seq_lens"][b]),
                                  toks, CFG.layers)
         np.testing.assert_allclose(nxt["logits"][b], ref, rtol=0, atol=1e-10)
+
+
+def test_m8_greedy_decoding_is_consistent_with_one_chain_pass():
+    """n one-token steps of greedy decoding against one pass over the chain
+    [root, t1, .., t_{n-1}]: the chain's argmax at node i is t_{i+1}, and the
+    caches agree (independent formulations: n sequential passes, one tree
+    pass)."""
+    w = model_weights(CFG)
+    wl = WL.replace(B=2, N=1, L_lo=25, L_hi=60)
+    x = model_inputs(CFG, wl)
+    n = 7
+    ar = oracle.ar_decode(CFG.dims(), w, x["k_cache"], x["v_cache"], x["seq_lens"],
+                          x["tokens"][:, 0], n)
+    chain_tok = np.concatenate([x["tokens"][:, :1], ar["tokens"][:, :n - 1]], axis=1)
+    chain = np.tile(np.arange(-1, n - 1), (wl.B, 1))
+    r = oracle.verify_pass(CFG.dims(), w, chain_tok, chain, x["seq_lens"], x["k_cache"],
+                           x["v_cache"])
+    np.testing.assert_array_equal(r["argmax"].reshape(wl.B, n), ar["tokens"])
+    np.testing.assert_array_equal(ar["seq_lens"], x["seq_lens"] + n)
+    for b in range(wl.B):
+        L = int(x["seq_lens"][b])
+        np.testing.assert_allclose(ar["k_cache"][:, b, :, L:L + n], r["k_cache"][:, b, :, L:L + n],
+                                   rtol=0, atol=1e-11)

@@ -35,6 +35,7 @@ class ModelConfig:
     eps: float = 1e-6
     theta: float = 1e6
     w_std: float = 0.02
+    lm_std: float | None = None   # LM-head std (w_std when None)
     seed: int = 0
 
     def dims(self, layers: int | None = None) -> dict:
@@ -52,6 +53,10 @@ MODELS = {
                             V=1000, seed=2002),
     "small_d128": ModelConfig("small_d128", layers=3, hidden=512, Hq=8, Hkv=2, D=128,
                               inter=768, V=3000, seed=2003),
+    # a small stack whose larger LM head spreads the logits (std about 4.5),
+    # so greedy choices are rarely near-ties: for multi-step decoding checks
+    "loop_d128": ModelConfig("loop_d128", layers=3, hidden=512, Hq=8, Hkv=2, D=128,
+                             inter=768, V=3000, lm_std=0.2, seed=2004),
 }
 
 _W_KEYS = ("embed", "ln1", "w_qkv", "q_norm", "k_norm", "w_o", "ln2", "w_gu", "w_down",
@@ -72,7 +77,8 @@ def model_weights(cfg: ModelConfig, layers: int | None = None) -> dict:
     qkv_rows = (cfg.Hq + 2 * cfg.Hkv) * cfg.D
     w = {}
     w["embed"] = _normal_bf16(top[0], cfg.V * Hd, 1.0).reshape(cfg.V, Hd)
-    w["lm_head"] = _normal_bf16(top[1], cfg.V * Hd, cfg.w_std).reshape(cfg.V, Hd)
+    lm_std = cfg.w_std if cfg.lm_std is None else cfg.lm_std
+    w["lm_head"] = _normal_bf16(top[1], cfg.V * Hd, lm_std).reshape(cfg.V, Hd)
     w["final_norm"] = _norm_weight(top[2], (Hd,))
     per = {k: [] for k in ("ln1", "w_qkv", "q_norm", "k_norm", "w_o", "ln2", "w_gu", "w_down")}
     for ly in range(Ly):
