@@ -12,11 +12,14 @@ from _helpers import i32_dev, to_dev, to_host_bits, to_host_f64
 pytestmark = pytest.mark.gpu
 
 # Tolerances of the pass (bf16 activations between kernels, fp32 accumulation)
-# against the fp64 oracle; see the design notes for their derivation.
-PASS_LOGITS_REL_L2 = 3e-2
-PASS_HIDDEN_REL_L2 = 3e-2
-PASS_CACHE_REL_L2 = 3e-2
-PASS_ARGMAX_GAP_EXEMPT = 5e-2
+# against the fp64 oracle.  They come from the oracle's own spread when every
+# activation the GPU rounds is perturbed by +-2^-9 (relative): 3.4e-3 at 3
+# layers and 1.18e-2 at 36 layers of the Qwen3-8B shape.
+SMALL_REL_L2 = 5e-3        # hidden, cache rows and logits of the 2-3 layer stacks
+SMALL_ARGMAX_GAP_EXEMPT = 1e-2
+FULL_HIDDEN_REL_L2 = 3e-2  # 36 layers
+FULL_CACHE_REL_L2 = 1e-2
+FULL_ARGMAX_GAP_EXEMPT = 5e-2
 
 Q8 = WORKLOADS["qwen3_8b_L1024_N64"]
 CASES = {
@@ -76,10 +79,10 @@ def test_pass_matches_oracle(name):
     gk, gv = to_host_f64(k), to_host_f64(v)
     rc = max(_rel(gk, ref["k_cache"]), _rel(gv, ref["v_cache"]))
     got = arg.cpu().numpy()
-    bad = (got != ref["argmax"]) & (ref["gap"] >= PASS_ARGMAX_GAP_EXEMPT)
+    bad = (got != ref["argmax"]) & (ref["gap"] >= SMALL_ARGMAX_GAP_EXEMPT)
     print(f"[pass] {name}: logits rel={rl:.2e} hidden rel={rh:.2e} cache rel={rc:.2e} "
           f"argmax diffs={(got != ref['argmax']).sum()} (non-exempt {bad.sum()})", flush=True)
-    assert rl <= PASS_LOGITS_REL_L2 and rh <= PASS_HIDDEN_REL_L2 and rc <= PASS_CACHE_REL_L2
+    assert rl <= SMALL_REL_L2 and rh <= SMALL_REL_L2 and rc <= SMALL_REL_L2
     assert not bad.any(), f"argmax differs at rows {np.nonzero(bad)[0]}"
     # rows the pass must not touch: prefix bits and the NaN rows past the tree
     kb = to_host_bits(k)
@@ -235,9 +238,9 @@ def test_pass_full_size_qwen3_8b(wname):
     print(f"[pass-full] {wname}: oracle done at {time.time() - t0:.0f} s", flush=True)
     rh = _rel(got_h.astype(np.float64), ref["hidden"])
     rc = max(_rel(gk, ref["k_cache"]), _rel(gv, ref["v_cache"]))
-    bad = (got != ref["argmax"]) & (ref["gap"] >= PASS_ARGMAX_GAP_EXEMPT)
+    bad = (got != ref["argmax"]) & (ref["gap"] >= FULL_ARGMAX_GAP_EXEMPT)
     print(f"[pass-full] {wname}: hidden rel={rh:.2e} cache rel={rc:.2e} argmax diffs="
           f"{(got != ref['argmax']).sum()} (non-exempt {bad.sum()}), min gap "
           f"{ref['gap'].min():.3e}", flush=True)
-    assert rh <= PASS_HIDDEN_REL_L2 and rc <= PASS_CACHE_REL_L2
+    assert rh <= FULL_HIDDEN_REL_L2 and rc <= FULL_CACHE_REL_L2
     assert not bad.any()
