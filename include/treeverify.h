@@ -141,9 +141,11 @@ int tv_tree_verify_attn_paged(const void* q, const void* k_pages,
  * workspace  at least tv_lmhead_argmax_workspace() bytes.  It must be
  *         zero-filled before its first use; every call leaves its first
  *         8*M (rounded up to 256) + 256 bytes zero-filled again when it
- *         completes (the rest, used when M > 64, is scratch), so one buffer
- *         serves any number of calls in stream order, of any M up to the size
- *         it was queried for (calls sharing it must not overlap).
+ *         completes.  When M > 64 a call also uses scratch at the end of the
+ *         buffer (ws_bytes counts), never inside the zero region of any M the
+ *         buffer was sized for; so one buffer serves any number of calls in
+ *         stream order, of any M up to the size it was queried for (calls
+ *         sharing it must not overlap).
  * Supported: bf16 needs K % 256 == 0; M >= 1, V >= 1.
  */
 size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype);
@@ -261,11 +263,10 @@ int tv_kv_compact_paged(void* k_pages, void* v_pages, const int32_t* block_table
  * argmax   [B*N] int32, row b*N + i
  * logits   [B*N][vocab] fp32 or NULL (for checking; not on the hot path)
  * hidden_out [B*N][hidden] fp32 or NULL: the final normalised hidden states
- * workspace  tv_verify_pass_workspace() bytes, zero-filled before its first
- *          use; the pass leaves its first part zero again (the LM-head
- *          contract), so a buffer serves any number of passes in stream
- *          order.  Nothing is allocated or memset: the pass may be captured
- *          with tv_graph_begin/tv_graph_end.
+ * workspace  tv_verify_pass_workspace() bytes of scratch (no initial
+ *          contents needed; one buffer serves passes of any shape up to the
+ *          size it was queried for, in stream order).  Nothing is allocated
+ *          or memset: the pass may be captured with tv_graph_begin/end.
  * Supported: D in {64, 128}; hidden, inter and Hq*D multiples of 256;
  *          hidden <= 16384; 1 <= N <= TV_MAX_NODES.  Device-side checks: TV_STATUS_BAD_PARENT,
  *          TV_STATUS_BAD_LEN, TV_STATUS_BAD_TOKEN (the token is read as 0).

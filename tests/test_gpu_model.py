@@ -244,3 +244,29 @@ def test_pass_full_size_qwen3_8b(wname):
           f"{ref['gap'].min():.3e}", flush=True)
     assert rh <= FULL_HIDDEN_REL_L2 and rc <= FULL_CACHE_REL_L2
     assert not bad.any()
+
+
+def test_pass_workspace_needs_no_initial_contents():
+    """One workspace, filled with 0xFF bytes, serves passes of different
+    shapes in turn (small then larger row counts and back)."""
+    import torch
+    import tree_draft_verification_amd as tv
+    runs = []
+    for name in ("small_d128_L300_N64", "small_d128_B3_N40_M120", "small_d128_L300_N64"):
+        mname, wl = CASES[name]
+        cfg = MODELS[mname]
+        runs.append((cfg, wl, model_weights(cfg), model_inputs(cfg, wl)))
+    model = _model_dev(runs[0][0], runs[0][2])
+    need = max(tv.tv_verify_pass_workspace(model, wl.B, wl.N, int(x["seq_lens"].max()))
+               for _, wl, _, x in runs)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    for cfg, wl, w, x in runs:
+        k, v = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
+        arg = tv.tv_verify_pass(model, i32_dev(x["tokens"]), i32_dev(x["parent"]),
+                                i32_dev(x["seq_lens"]), k, v,
+                                max_seq_len=int(x["seq_lens"].max()), workspace=ws)
+        ref = oracle.verify_pass(cfg.dims(), w, x["tokens"], x["parent"], x["seq_lens"],
+                                 x["k_cache"], x["v_cache"], logit_rows=[])
+        got = arg.cpu().numpy()
+        bad = (got != ref["argmax"]) & (ref["gap"] >= SMALL_ARGMAX_GAP_EXEMPT)
+        assert not bad.any(), f"{wl.B}x{wl.N}: argmax differs at rows {np.nonzero(bad)[0]}"

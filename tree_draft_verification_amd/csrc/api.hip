@@ -155,7 +155,8 @@ int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax, float* 
   if (blocks > 2147483647LL) return TV_ENOTSUP;
   if (!workspace || ws_bytes < tv::lmhead_ws_bytes(M, K, V, dtype)) return TV_EWORKSPACE;
   return hip_status(tv::launch_lmhead_argmax(hidden, w, argmax, logits, M, K, V, dtype, w_layout,
-                                             workspace, static_cast<hipStream_t>(stream)));
+                                             workspace, ws_bytes,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 int tv_tree_accept(const int32_t* parent, const int32_t* draft_tokens,

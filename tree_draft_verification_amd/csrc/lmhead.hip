@@ -408,9 +408,12 @@ __global__ __launch_bounds__(kThreads) void lmhead_f32_kernel(
 static int lmhead_mb(int M) { return M <= 64 ? 4 : 8; }
 
 // Workspace: per-row keys, then the completion counter on its own 256-byte
-// line (this region is zero between calls), then - for the partial-key form
-// only - one key per (row, vocabulary tile), overwritten by every call.
-static size_t lmhead_zero_bytes(int M) { return ((size_t)M * 8 + 255) / 256 * 256 + 256; }
+// line (this region is zero between calls); for the partial-key form (M >
+// 64), one key per (row, vocabulary tile) at the END of the caller's buffer,
+// overwritten by every call.  At the end, a call's partial keys never land
+// inside the zero region of a later call with more rows (the buffer holds
+// that call's zero region plus at least as many partial keys).
+size_t lmhead_zero_bytes(int M) { return ((size_t)M * 8 + 255) / 256 * 256 + 256; }
 
 size_t lmhead_ws_bytes(int M, int /*K*/, int V, int dtype) {
   size_t bytes = lmhead_zero_bytes(M);
@@ -431,7 +434,7 @@ hipError_t launch_lmhead_pack(const void* w, void* packed, int V, int K, hipStre
 
 hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
                                 float* logits, int M, int K, int V, int dtype, int w_layout,
-                                void* ws, hipStream_t stream) {
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
   unsigned long long* keys = static_cast<unsigned long long*>(ws);
   unsigned* counter = reinterpret_cast<unsigned*>(static_cast<char*>(ws) +
                                                   ((size_t)M * 8 + 255) / 256 * 256);
@@ -452,8 +455,19 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
   const bf16_t* wv = static_cast<const bf16_t*>(w);
   const bool pk = w_layout == TV_LAYOUT_PACKED;
   const dim3 grid(total), block(kThreads);
-  if (mb != 4)
-    keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + lmhead_zero_bytes(M));
+  if (mb != 4) {
+    const size_t pbytes = (size_t)M * (pk ? gemm32_vtiles(V) : nvt) * 8;
+    keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
+                                                 ((ws_bytes - pbytes) & ~(size_t)255));
+  }
+  if (mb != 4 && pk) {
+    // many rows: the matrix-core tiling (256-row W tiles), then the reduce
+    hipError_t e = launch_gemm32_argmax(h, wv, keys, logits, M, K, V, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(argmax_reduce_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, keys,
+                       argmax, M, gemm32_vtiles(V));
+    return hipGetLastError();
+  }
 #define TV_LM_LAUNCH(P, MBV, MODEV)                                                         \
   hipLaunchKernelGGL((lmhead_bf16_kernel<P, MBV, MODEV>), grid, block, 0, stream, h, wv, argmax, \
                      logits, keys, counter, M, K, V, nmt, total, nullptr, 1)
@@ -481,6 +495,7 @@ static int proj_ring(int M, int K) {
 // grid runs at the speed of its doubled CUs: measured 40% slower at 320
 // workgroups than at 256 for the 4096 x 4096 case).
 int proj_splits(int M, int K, int Nout) {
+  if (lmhead_mb(M) != 4) return gemm32_splits(M, K, Nout);
   const int nmt = (M + 16 * lmhead_mb(M) - 1) / (16 * lmhead_mb(M));
   const int tiles = nmt * ((Nout + kVT - 1) / kVT);
   const int ngroup = K / (kKC * proj_ring(M, K));
@@ -493,6 +508,7 @@ int proj_splits(int M, int K, int Nout) {
 hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, int M, int K,
                        int Nout, int nsplit, hipStream_t stream) {
   const int mb = lmhead_mb(M);
+  if (mb != 4) return launch_gemm32_store(hidden, w_packed, part, M, K, Nout, nsplit, stream);
   const int nmt = (M + 16 * mb - 1) / (16 * mb);
   const int total = nmt * ((Nout + kVT - 1) / kVT) * nsplit;
   const bf16_t* h = static_cast<const bf16_t*>(hidden);

@@ -57,17 +57,22 @@ __device__ __forceinline__ void flag(int32_t* st, int b, int f) {
 // per node row m = b*N + i).  pos[m] = L_b + depth(i), or -1 when the length
 // of sequence b or the root path of node i is malformed (a row with pos -1 is
 // never written to the caches).
+// Workgroup 0 also clears the LM head's key region of the workspace (the LM
+// head needs it zero and leaves it zero; clearing it here makes the pass
+// independent of what earlier calls with other shapes left in the buffer).
 __global__ __launch_bounds__(256) void prep_kernel(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ seq_lens, const bf16_t* __restrict__ embed,
     const bf16_t* __restrict__ ln1, float* __restrict__ x, bf16_t* __restrict__ h,
     int32_t* __restrict__ pos, int32_t* __restrict__ dev_status, int N, int hidden, int V,
-    int Lcap, int max_seq_len, float eps) {
+    int Lcap, int max_seq_len, float eps, uint32_t* __restrict__ lm_zero, int lm_zero_words) {
   __shared__ float s_red[4];
   const int m = blockIdx.x;
   const int b = m / N;
   const int i = m - b * N;
   const int tid = threadIdx.x;
+  if (m == 0)
+    for (int w = tid; w < lm_zero_words; w += 256) lm_zero[w] = 0u;
   if (tid == 0) {
     const int32_t* par = parent + (size_t)b * N;
     const int L = seq_lens[b];
@@ -341,7 +346,8 @@ hipError_t launch_verify_pass(const tv_model_dims& d, const tv_model_weights& w,
 
   hipLaunchKernelGGL(prep_kernel, dim3(M), dim3(256), 0, stream, tokens, parent, seq_lens,
                      static_cast<const bf16_t*>(w.embed), ln1, x, gin, pos, dev_status, N,
-                     d.hidden, d.vocab, Lcap, max_seq_len, d.rms_eps);
+                     d.hidden, d.vocab, Lcap, max_seq_len, d.rms_eps,
+                     reinterpret_cast<uint32_t*>(base + p.off_lm), (int)(lmhead_zero_bytes(M) / 4));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int heads = d.Hq + 2 * d.Hkv;
   for (int ly = 0; ly < d.layers; ++ly) {
@@ -381,7 +387,7 @@ hipError_t launch_verify_pass(const tv_model_dims& d, const tv_model_weights& w,
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_lmhead_argmax(gin, w.lm_head, argmax, logits, M, d.hidden, d.vocab, TV_BF16,
-                              TV_LAYOUT_PACKED, base + p.off_lm, stream);
+                              TV_LAYOUT_PACKED, base + p.off_lm, p.off_pos - p.off_lm, stream);
 }
 
 }  // namespace tv

@@ -106,9 +106,11 @@ size_t lmhead_packed_bytes(int V, int K);
 
 hipError_t launch_lmhead_pack(const void* w, void* packed, int V, int K, hipStream_t stream);
 
+// The first lmhead_zero_bytes(M) bytes of ws must be zero and are left zero.
+size_t lmhead_zero_bytes(int M);
 hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
                                 float* logits, int M, int K, int V, int dtype, int w_layout,
-                                void* ws, hipStream_t stream);
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 hipError_t launch_tree_accept(const int32_t* parent, const int32_t* draft,
                               const int32_t* tgt, int32_t* path, int32_t* path_len,
@@ -120,6 +122,16 @@ hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t*
                              int Lcap, int P, int dtype, hipStream_t stream,
                              const int32_t* block_table = nullptr, int max_blocks = 0,
                              int page_size = 0, int num_pages = 0);
+
+// ---------------------------------------------------------------- products with M > 64 rows
+
+int gemm32_vtiles(int V);                  // 256-row W tiles
+int gemm32_splits(int M, int K, int Nout);
+hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
+                                unsigned long long* keys, float* logits, int M, int K, int V,
+                                hipStream_t stream);
+hipError_t launch_gemm32_store(const void* hidden, const void* w_packed, float* part, int M,
+                               int K, int Nout, int nsplit, hipStream_t stream);
 
 // ---------------------------------------------------------------- projections
 
