@@ -322,18 +322,37 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
+  // Tile loads.  The 128-row variant issues a tile's loads back to back and
+  // does not hold them across the products (its registers are full; with two
+  // workgroups per CU, one workgroup's loads overlap another's products).
+  // The 64-row variant has registers to spare and runs at small sizes with
+  // few workgroups per CU, so it issues the next tile's loads right after
+  // staging the current one and hides their latency behind the products.
+  constexpr bool kPrefetch = (QBW == 1);
+  if constexpr (kPrefetch) {
+    __syncthreads();  // tree tile list (and page entries) visible
+    if (n_tiles > 0) {
+      int k0r, n0, t0;
+      tile_rows(0, k0r, n0, t0);
+      load_tile(k0r, n0, t0 >= 0);
+    }
+  }
   for (int it = 0; it < n_tiles; ++it) {
     int krow0, nvalid, tt;
     __syncthreads();  // previous tile consumed (first trip: tree tile list visible)
     tile_rows(it, krow0, nvalid, tt);
     const bool tree = tt >= 0;
     const bool need_mask = tree || nvalid < kKT;
-    // Load the tile and stage it in LDS.  The loads are issued back to back
-    // and are not held across the products: with two or more workgroups per
-    // CU, one workgroup's loads overlap another's products.
-    load_tile(krow0, nvalid, tree);
+    if constexpr (!kPrefetch) load_tile(krow0, nvalid, tree);
     store_tile();
     __syncthreads();  // this tile is in LDS
+    if constexpr (kPrefetch) {
+      if (it + 1 < n_tiles) {
+        int k1r, n1, t1;
+        tile_rows(it + 1, k1r, n1, t1);
+        load_tile(k1r, n1, t1 >= 0);
+      }
+    }
 
     // S^T = K Q^T: lane holds query column l16, keys kb*16 + 4*kg + r.
     f32x4_t s[QBW][4];

@@ -101,7 +101,12 @@ enum : int {
 // wavefront): 2 where several workgroups share a CU (the LM head), 4 for the
 // projections, which run about one workgroup per CU and need the deeper
 // pipeline to keep enough bytes in flight.
-template <bool PACKED, int MB, int MODE, int RING = 2>
+//
+// HD is the depth of the H stage prefetch: 1 loads a chunk's H slice while
+// the previous chunk is multiplied; deeper rings keep HD chunks in flight
+// (projections: one workgroup per CU, so an H load's L2 latency is not
+// hidden by other workgroups).  A trip covers max(RING, HD) chunks.
+template <bool PACKED, int MB, int MODE, int RING = 2, int HD = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MB == 4 ? 2 : 1)))
 void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
                         int32_t* __restrict__ argmax, float* __restrict__ logits,
@@ -128,10 +133,11 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
   const int m0 = mt * kRowsM;
   const int v0 = vt * kVT;
   const int nk = K / kKC;
-  // this split's k chunks [cb, cb + nkl): whole groups of RING chunks
-  const int ngroup = nk / RING;
-  const int cb = RING * (ks * ngroup / nsplit);
-  const int nkl = RING * ((ks + 1) * ngroup / nsplit) - cb;
+  // this split's k chunks [cb, cb + nkl): whole groups of TRIP chunks
+  constexpr int TRIP = RING > HD ? RING : HD;
+  const int ngroup = nk / TRIP;
+  const int cb = TRIP * (ks * ngroup / nsplit);
+  const int nkl = TRIP * ((ks + 1) * ngroup / nsplit) - cb;
 
   // W source of this lane (clamped rows in the row-major layout; the packed
   // layout is zero-padded to whole tiles)
@@ -169,7 +175,7 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
   }
 
   u32x4_t wb[RING][2][4];  // [ring slot][16-row block][piece]
-  uint4 hreg[HP];
+  u32x4_t hreg[HD][HP];    // [H slot: chunk % HD][piece]
 #pragma unroll
   for (int d = 0; d < RING; ++d)
 #pragma unroll
@@ -177,9 +183,17 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 #pragma unroll
       for (int s = 0; s < 4; ++s) wb[d][vb][s] = wload(cb + min(d, nkl - 1), vb, s);
 #pragma unroll
-  for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i] + cb * kKC);
+  for (int d = 0; d < HD; ++d)
 #pragma unroll
-  for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(&sH[0][hdst[i]]) = hreg[i];
+    for (int i = 0; i < HP; ++i)
+      hreg[d][i] = *reinterpret_cast<const u32x4_t*>(hsrc[i] + (cb + min(d, nkl - 1)) * kKC);
+#pragma unroll
+  for (int i = 0; i < HP; ++i) *reinterpret_cast<u32x4_t*>(&sH[0][hdst[i]]) = hreg[0][i];
+  if constexpr (HD > 1) {  // slot 0 is free again: chunk HD goes there
+#pragma unroll
+    for (int i = 0; i < HP; ++i)
+      hreg[0][i] = *reinterpret_cast<const u32x4_t*>(hsrc[i] + (cb + min(HD, nkl - 1)) * kKC);
+  }
   __syncthreads();
 
   f32x4_t acc[2][MB];
@@ -188,16 +202,18 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // nkl is a multiple of RING (K is a multiple of 256, splits take whole
-  // groups): RING chunks per trip keep the ring slot and the LDS buffer
+  // nkl is a multiple of TRIP (K is a multiple of 256, splits take whole
+  // groups): TRIP chunks per trip keep the ring slots and the LDS buffer
   // compile-time constants.
-  for (int c0 = 0; c0 < nkl; c0 += RING) {
+  for (int c0 = 0; c0 < nkl; c0 += TRIP) {
 #pragma unroll
-    for (int u = 0; u < RING; ++u) {
+    for (int u = 0; u < TRIP; ++u) {
       const int c = c0 + u;
-      const int ch = cb + min(c + 1, nkl - 1);
+      if constexpr (HD == 1) {
+        const int ch = cb + min(c + 1, nkl - 1);
 #pragma unroll
-      for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const uint4*>(hsrc[i] + ch * kKC);
+        for (int i = 0; i < HP; ++i) hreg[0][i] = *reinterpret_cast<const u32x4_t*>(hsrc[i] + ch * kKC);
+      }
       const bf16_t* sh = sH[u & 1];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -208,7 +224,7 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 #pragma unroll
           for (int vb = 0; vb < 2; ++vb) {
             Frag8 wf;
-            wf.q = wb[u][vb][s];
+            wf.q = wb[u % RING][vb][s];
             acc[vb][mb] = mfma16x16x32(wf.v, hf.v, acc[vb][mb]);
           }
         }
@@ -217,9 +233,17 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 #pragma unroll
       for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) wb[u][vb][s] = wload(cw, vb, s);
+        for (int s = 0; s < 4; ++s) wb[u % RING][vb][s] = wload(cw, vb, s);
+      // chunk c+1's H slice (slot (c+1) % HD) into the other LDS buffer;
+      // with HD > 1 that slot then takes chunk c+1+HD
+      const int hs = HD == 1 ? 0 : (u + 1) % HD;  // constant once unrolled
 #pragma unroll
-      for (int i = 0; i < HP; ++i) *reinterpret_cast<uint4*>(&sH[(u & 1) ^ 1][hdst[i]]) = hreg[i];
+      for (int i = 0; i < HP; ++i) *reinterpret_cast<u32x4_t*>(&sH[(u & 1) ^ 1][hdst[i]]) = hreg[hs][i];
+      if constexpr (HD > 1) {
+        const int cn = cb + min(c + 1 + HD, nkl - 1);
+#pragma unroll
+        for (int i = 0; i < HP; ++i) hreg[hs][i] = *reinterpret_cast<const u32x4_t*>(hsrc[i] + cn * kKC);
+      }
       __syncthreads();
     }
   }
@@ -484,8 +508,9 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
   return hipGetLastError();
 }
 
-// Ring depth of the projection kernel: 4 for one row block when K holds whole
-// groups of four chunks, else 2.
+// Chunks per trip of the projection kernel (one row block): 4 (two-deep W
+// ring, four-deep H prefetch) when K holds whole groups of four chunks,
+// else 2 (both two-deep).
 static int proj_ring(int M, int K) {
   return lmhead_mb(M) == 4 && (K / kKC) % 4 == 0 ? 4 : 2;
 }
@@ -514,11 +539,11 @@ hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, in
   const bf16_t* h = static_cast<const bf16_t*>(hidden);
   const bf16_t* wv = static_cast<const bf16_t*>(w_packed);
   if (mb == 4 && proj_ring(M, K) == 4)
-    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 4>), dim3(total),
+    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 2, 4>), dim3(total),
                        dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
                        K, Nout, nmt, total, part, nsplit);
   else if (mb == 4)
-    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 2>), dim3(total),
+    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 2, 2>), dim3(total),
                        dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
                        K, Nout, nmt, total, part, nsplit);
   else
