@@ -5,9 +5,10 @@ One step = tv_tree_verify_attn -> tv_lmhead_argmax -> tv_tree_accept ->
 tv_kv_compact on one stream, over one batch of synthetic inputs already
 resident in HBM (the Qwen3-8B-shaped layer with a 1024-token prefix and a
 64-node draft tree by default).  Prints one JSON line with verified tree
-nodes/s, the step time, the roofline fraction of the dominant kernel (the
-LM head, whose per-launch time is taken with HIP events on the launch
-stream), and the fp64 oracle timed on this host's cores as a CPU baseline.
+nodes/s of the step captured once as a HIP graph and replayed, the step
+time, the roofline fraction of the dominant kernel (the LM head, whose
+per-launch time is taken with HIP events on the launch stream in eager
+steps), and the fp64 oracle timed on this host's cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--paged PAGE_SIZE] [--model qwen3_8b] [--tree CONFIG]
@@ -256,11 +257,34 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    # Eager steps, each call bracketed by HIP events on the stream it is
+    # launched on: the per-kernel breakdown and the LM head's own time.
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+
+    # The value: the same step captured once as a HIP graph and replayed
+    # (no host launch gaps between the four calls).
+    gs = torch.cuda.Stream()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    with torch.cuda.stream(gs):
+        step()
+        gs.synchronize()
+        tv.tv_graph_begin(gs)
+        step()
+        graph = tv.tv_graph_end(gs)
+        for _ in range(args.warmup):
+            graph.launch(gs)
+        gs.synchronize()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            gev[i][0].record(gs)
+            graph.launch(gs)
+            gev[i][1].record(gs)
+        gs.synchronize()
+        t1 = time.perf_counter()
+    graph_per = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in gev])
 
     # For reference only: the same LM head reading the row-major weight.
     rm_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -275,7 +299,8 @@ def main():
     names = ["attn", "lmhead", "accept", "compact"]
     per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            * 1e3 for j, n in enumerate(names)}
-    step_us = float(np.mean([ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)])) * 1e3
+    eager_us = float(np.mean([ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)])) * 1e3
+    step_us = float(np.median(graph_per))
     wall_ms = (t1 - t0) * 1e3 / args.steps
     value = wl.M * args.steps / (t1 - t0)
 
@@ -317,6 +342,9 @@ def main():
                    "kv_layout": f"paged{ps}" if ps else "contiguous",
                    "parallelism": "none (1 GPU)"},
         "step_us": round(step_us, 2),
+        "step_us_p10_p90": [round(float(np.percentile(graph_per, 10)), 2),
+                            round(float(np.percentile(graph_per, 90)), 2)],
+        "eager_step_us": round(eager_us, 2),
         "mean_path_len": float(plen_h.mean()),
         "roofline": roof,
         "kernels": kernels,
