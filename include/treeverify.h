@@ -168,6 +168,21 @@ int tv_lmhead_pack_weights(const void* w, void* w_packed, int V, int K,
                            int dtype, void* stream);
 
 /*
+ * Pack a gate/up weight of the multi-layer pass's MLP (the SwiGLU of the
+ * Qwen3 targets named in the JetSpec abstract): w is [2 inter][K] bf16
+ * row-major, the inter gate rows, then the inter up rows.  The result has
+ * the tv_lmhead_pack_weights layout of a [2 inter][K] weight whose rows are
+ * interleaved per 128-row tile: packed rows 128 t .. 128 t + 63 are gate
+ * rows 64 t .. 64 t + 63 and packed rows 128 t + 64 .. 128 t + 127 the up
+ * rows of the same features, so one workgroup holds both halves of the
+ * features it produces.  w_packed: tv_lmhead_packed_bytes(2 inter, K, dtype)
+ * bytes, caller-owned, not overlapping w.  Returns TV_ENOTSUP unless dtype is
+ * TV_BF16, K % 256 == 0 and inter % 64 == 0.
+ */
+int tv_pack_gate_up_weights(const void* w, void* w_packed, int inter, int K,
+                            int dtype, void* stream);
+
+/*
  * Greedy longest-accepted-path selection plus the bonus token (JetSpec GitHub
  * README, "JetSpec > Overview": lossless by construction).
  *
@@ -248,14 +263,16 @@ int tv_kv_compact_paged(void* k_pages, void* v_pages, const int32_t* block_table
  *            w_qkv      layers x packed([(Hq + 2 Hkv) D] rows, K = hidden):
  *                       q rows (head-major), then k rows, then v rows
  *            w_o        layers x packed([hidden] rows, K = Hq D)
- *            w_gu       layers x packed([2 inter] rows, K = hidden): gate
- *                       rows, then up rows
+ *            w_gu       layers x packed_gu([2 inter] rows, K = hidden): the
+ *                       tv_pack_gate_up_weights layout (gate and up rows
+ *                       interleaved per 128-row tile)
  *            w_down     layers x packed([hidden] rows, K = inter)
  *            final_norm [hidden]
  *            lm_head    packed([vocab] rows, K = hidden)
  *          "packed(r, K)" is the tv_lmhead_pack_weights layout of an [r][K]
- *          row-major weight, tv_lmhead_packed_bytes(r, K, TV_BF16) bytes;
- *          the layers' blocks follow each other without gaps.
+ *          row-major weight, tv_lmhead_packed_bytes(r, K, TV_BF16) bytes
+ *          (packed_gu the same size); the layers' blocks follow each other
+ *          without gaps.
  * tokens, parent  [B][N] int32; seq_lens [B] (read only: the caller runs
  *          tv_tree_accept and tv_kv_compact_layers afterwards)
  * k_cache, v_cache  [layers][B][Hkv][Lcap][D] bf16: prefix rows read, tree

@@ -39,7 +39,7 @@ def test_header_declares_the_four_calls():
     names = _declared_functions()
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
-              "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
+              "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights", "tv_pack_gate_up_weights",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
               "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
@@ -123,6 +123,13 @@ def test_pack_host_validation(lib):
     assert p(FAKE, ctypes.c_void_p(0x2000), 0, 256, 0, None) == -1
     assert p(FAKE, ctypes.c_void_p(0x2000), 1000, 384, 0, None) == -2
     assert p(FAKE, ctypes.c_void_p(0x2000), 1000, 256, 1, None) == -2
+    g = lib.tv_pack_gate_up_weights
+    assert g(None, FAKE, 512, 256, 0, None) == -1
+    assert g(FAKE, FAKE, 512, 256, 0, None) == -1                          # in place
+    assert g(FAKE, ctypes.c_void_p(0x2000), 0, 256, 0, None) == -1
+    assert g(FAKE, ctypes.c_void_p(0x2000), 500, 256, 0, None) == -2        # inter % 64
+    assert g(FAKE, ctypes.c_void_p(0x2000), 512, 384, 0, None) == -2
+    assert g(FAKE, ctypes.c_void_p(0x2000), 512, 256, 1, None) == -2
 
 
 def test_accept_and_compact_host_validation(lib):
@@ -246,7 +253,7 @@ def test_binding_names_match_the_c_calls():
     import tree_draft_verification_amd as tv
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
-              "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights",
+              "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights", "tv_pack_gate_up_weights",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
               "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",

@@ -28,6 +28,8 @@ CASES = {
     "small_d128_L300_N64": ("small_d128", Q8.replace(Hq=8, Hkv=2, L_lo=300, L_hi=300, seed=61)),
     "small_d128_B3_N40_M120": ("small_d128", WORKLOADS["qwen3_8b_ragged8_N64"].replace(
         B=3, Hq=8, Hkv=2, N=40, L_lo=10, L_hi=200, seed=62)),
+    # unsplit gate/up projection with the fused silu(gate) * up epilogue
+    "wide_mlp_N64_L200": ("wide_mlp", Q8.replace(Hq=2, Hkv=1, L_lo=200, L_hi=200, seed=63)),
 }
 
 

@@ -39,7 +39,7 @@ def _lib_handle():
 __all__ = [
     "TreeVerifyError", "tv_tree_verify_attn", "tv_tree_verify_attn_workspace",
     "tv_lmhead_argmax", "tv_lmhead_argmax_workspace", "tv_lmhead_packed_bytes",
-    "tv_lmhead_pack_weights", "PackedWeights", "tv_tree_accept",
+    "tv_lmhead_pack_weights", "tv_pack_gate_up_weights", "PackedWeights", "tv_tree_accept",
     "tv_kv_compact", "tv_status_string", "tv_abi_version", "library_path",
     "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace", "tv_kv_compact_paged",
     "Model", "tv_model_pack", "tv_verify_pass", "tv_verify_pass_workspace",
@@ -232,6 +232,23 @@ def tv_lmhead_pack_weights(w: torch.Tensor) -> PackedWeights:
     return PackedWeights(out, V, K, w.dtype)
 
 
+def tv_pack_gate_up_weights(w: torch.Tensor) -> torch.Tensor:
+    """Pack a [2 inter, K] bf16 gate/up weight (gate rows, then up rows) with
+    gate and up rows interleaved per 128-row tile; returns the uint8 buffer."""
+    R, K = w.shape
+    if R % 2:
+        raise ValueError("a gate/up weight has an even number of rows")
+    dt = _dtype_code(w)
+    nbytes = tv_lmhead_packed_bytes(R, K, dt)
+    if nbytes == 0:
+        raise TreeVerifyError("tv_pack_gate_up_weights", _lib.TV_ENOTSUP)
+    out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    st = _lib_handle().tv_pack_gate_up_weights(_ptr(w.contiguous()), _ptr(out), R // 2, K, dt,
+                                               _stream(w.device))
+    _check("tv_pack_gate_up_weights", st)
+    return out
+
+
 def tv_lmhead_argmax(hidden, w, argmax=None, logits=None, *,
                      workspace: torch.Tensor | None = None) -> torch.Tensor:
     """argmax[r] = argmax_v sum_k hidden[r,k] w[v,k].  hidden [M,K]; w [V,K]
@@ -353,7 +370,8 @@ def tv_model_pack(dims: dict, w: dict) -> Model:
     w_qkv [layers,(Hq+2Hkv)D,hidden], w_o [layers,hidden,Hq D],
     w_gu [layers,2 inter,hidden], w_down [layers,hidden,inter],
     final_norm [hidden], lm_head [V,hidden].  Each projection of each layer is
-    repacked with tv_lmhead_pack_weights into one buffer per projection.
+    repacked with tv_lmhead_pack_weights (w_gu with tv_pack_gate_up_weights)
+    into one buffer per projection.
     """
     bufs = {k: w[k].contiguous() for k in ("embed", "ln1", "ln2", "q_norm", "k_norm",
                                             "final_norm")}
@@ -366,9 +384,14 @@ def tv_model_pack(dims: dict, w: dict) -> Model:
         out = torch.empty(Ly * per, dtype=torch.uint8, device=t.device)
         for ly in range(Ly):
             src = t[ly].contiguous()
-            st = _lib_handle().tv_lmhead_pack_weights(_ptr(src), out.data_ptr() + ly * per, R, K,
-                                                      TV_BF16, _stream(t.device))
-            _check("tv_lmhead_pack_weights", st)
+            if k == "w_gu":
+                st = _lib_handle().tv_pack_gate_up_weights(_ptr(src), out.data_ptr() + ly * per,
+                                                           R // 2, K, TV_BF16, _stream(t.device))
+                _check("tv_pack_gate_up_weights", st)
+            else:
+                st = _lib_handle().tv_lmhead_pack_weights(_ptr(src), out.data_ptr() + ly * per,
+                                                          R, K, TV_BF16, _stream(t.device))
+                _check("tv_lmhead_pack_weights", st)
         bufs[k] = out
     bufs["lm_head"] = tv_lmhead_pack_weights(w["lm_head"]).data
     return Model(dims, bufs)

@@ -46,6 +46,7 @@ SIGNATURES = {
     "tv_lmhead_argmax": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
     "tv_lmhead_packed_bytes": (_sz, [_i, _i, _i]),
     "tv_lmhead_pack_weights": (_i, [_p, _p, _i, _i, _i, _p]),
+    "tv_pack_gate_up_weights": (_i, [_p, _p, _i, _i, _i, _p]),
     "tv_tree_accept": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p]),
     "tv_kv_compact": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "tv_verify_pass_workspace": (_sz, [_pd, _i, _i, _i]),

@@ -140,6 +140,15 @@ int tv_lmhead_pack_weights(const void* w, void* w_packed, int V, int K, int dtyp
   return hip_status(tv::launch_lmhead_pack(w, w_packed, V, K, static_cast<hipStream_t>(stream)));
 }
 
+int tv_pack_gate_up_weights(const void* w, void* w_packed, int inter, int K, int dtype,
+                            void* stream) {
+  if (!w || !w_packed || w == w_packed) return TV_EINVAL;
+  if (inter < 1 || K < 1) return TV_EINVAL;
+  if (dtype != TV_BF16 || K % 256 || inter % 64) return TV_ENOTSUP;
+  return hip_status(
+      tv::launch_pack_gate_up(w, w_packed, inter, K, static_cast<hipStream_t>(stream)));
+}
+
 int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax, float* logits, int M,
                      int K, int V, int dtype, int w_layout, void* workspace, size_t ws_bytes,
                      void* stream) {

@@ -90,6 +90,7 @@ enum : int {
   kArgmaxCommit = 0,   // fold per-row keys into the global keys (M <= 64)
   kArgmaxPartial = 1,  // write one key per (row, vocabulary tile)
   kStorePartial = 2,   // write the fp32 partial sums of its k range (projections)
+  kSwiGLU = 3,         // gate/up projection, whole k range: write bf16 silu(gate) * up
 };
 
 // MODE kStorePartial computes out = H W^T for a linear layer (V = output
@@ -112,7 +113,7 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
                         int32_t* __restrict__ argmax, float* __restrict__ logits,
                         unsigned long long* __restrict__ keys, unsigned* __restrict__ counter,
                         int M, int K, int V, int nmt, int total_blocks, float* __restrict__ part,
-                        int nsplit) {
+                        int nsplit, bf16_t* __restrict__ act, int inter) {
   constexpr int kRowsM = 16 * MB;                  // hidden-state rows per workgroup
   constexpr int HP = kRowsM * (kKC / 8) / kThreads;  // 16-byte H pieces per thread per stage
   __shared__ __attribute__((aligned(16))) bf16_t sH[2][kRowsM * kHRow];
@@ -250,6 +251,47 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
 
   // ---- epilogue: lane holds rows v = v0 + wave*32 + vb*16 + 4*kg + r of
   // hidden-state row m = m0 + mb*16 + l16
+  if constexpr (MODE == kSwiGLU) {
+    // Gate/up rows are packed interleaved (each 128-row tile: gate rows of
+    // features 64 vt .. 64 vt + 63, then the up rows of the same features),
+    // so wavefronts 2 and 3 hold the up values matching wavefronts 0 and 1
+    // lane for lane.  They pass them through LDS; 0 and 1 write
+    // a[m][f] = bf16(silu(gate) * up), the expression of the split form's
+    // epilogue kernel.
+    float* su = reinterpret_cast<float*>(&sH[0][0]);  // [2][2][MB][64][4] floats
+    __syncthreads();  // every wavefront is past its last read of sH
+    if (wave >= 2) {
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          *reinterpret_cast<f32x4_t*>(&su[((((wave - 2) * 2 + vb) * MB + mb) * 64 + lane) * 4]) =
+              acc[vb][mb];
+    }
+    __syncthreads();
+    if (wave < 2) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int m = m0 + mb * 16 + l16;
+        if (m >= M) continue;
+#pragma unroll
+        for (int vb = 0; vb < 2; ++vb) {
+          const f32x4_t u =
+              *reinterpret_cast<const f32x4_t*>(&su[(((wave * 2 + vb) * MB + mb) * 64 + lane) * 4]);
+          const f32x4_t g = acc[vb][mb];
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = g[e] / (1.f + __expf(-g[e])) * u[e];
+          const int f = 64 * vt + wave * 32 + vb * 16 + 4 * kg;
+          u32x2_t pk;
+          pk.x = f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16);
+          pk.y = f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16);
+          *reinterpret_cast<u32x2_t*>(act + (size_t)m * inter + f) = pk;
+        }
+      }
+    }
+    return;
+  }
   if constexpr (MODE == kStorePartial) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -340,9 +382,12 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const unsigned long 
 
 // Row-major [V][K] -> packed layout; one thread per 16-byte packed piece,
 // rows past V written as zeros.
+// With inter > 0 the rows are a gate/up weight [2 inter][K] (gate rows, then
+// up rows) and are packed interleaved: packed row 128 t + j is gate row
+// 64 t + j (j < 64) or up row 64 t + j - 64 (j >= 64).
 __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ W,
                                                    bf16_t* __restrict__ P, int K, int V,
-                                                   size_t pieces) {
+                                                   size_t pieces, int inter) {
   const int nk = K / kKC;
   for (size_t p = (size_t)blockIdx.x * blockDim.x + threadIdx.x; p < pieces;
        p += (size_t)gridDim.x * blockDim.x) {
@@ -355,9 +400,13 @@ __global__ __launch_bounds__(256) void pack_kernel(const bf16_t* __restrict__ W,
     t /= 8;
     const int c = (int)(t % nk);
     const size_t vt = t / nk;
-    const size_t row = vt * kVT + j * 16 + (lane & 15);
+    size_t row = vt * kVT + j * 16 + (lane & 15);
     const int col = c * kKC + 32 * (lane >> 4) + 8 * s;
     uint4 val = make_uint4(0, 0, 0, 0);
+    if (inter > 0) {
+      const size_t jr = row % kVT;
+      row = jr < 64 ? 64 * vt + jr : (size_t)inter + 64 * vt + (jr - 64);
+    }
     if (row < (size_t)V) val = *reinterpret_cast<const uint4*>(W + row * K + col);
     reinterpret_cast<uint4*>(P)[p] = val;
   }
@@ -452,7 +501,16 @@ size_t lmhead_packed_bytes(int V, int K) {
 hipError_t launch_lmhead_pack(const void* w, void* packed, int V, int K, hipStream_t stream) {
   const size_t pieces = lmhead_packed_bytes(V, K) / 16;
   hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, stream,
-                     static_cast<const bf16_t*>(w), static_cast<bf16_t*>(packed), K, V, pieces);
+                     static_cast<const bf16_t*>(w), static_cast<bf16_t*>(packed), K, V, pieces, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_gate_up(const void* w, void* packed, int inter, int K,
+                               hipStream_t stream) {
+  const size_t pieces = lmhead_packed_bytes(2 * inter, K) / 16;
+  hipLaunchKernelGGL(pack_kernel, dim3(4096), dim3(256), 0, stream,
+                     static_cast<const bf16_t*>(w), static_cast<bf16_t*>(packed), K, 2 * inter,
+                     pieces, inter);
   return hipGetLastError();
 }
 
@@ -494,7 +552,7 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
   }
 #define TV_LM_LAUNCH(P, MBV, MODEV)                                                         \
   hipLaunchKernelGGL((lmhead_bf16_kernel<P, MBV, MODEV>), grid, block, 0, stream, h, wv, argmax, \
-                     logits, keys, counter, M, K, V, nmt, total, nullptr, 1)
+                     logits, keys, counter, M, K, V, nmt, total, nullptr, 1, nullptr, 0)
   if (mb == 4) {
     if (pk) TV_LM_LAUNCH(true, 4, kArgmaxCommit); else TV_LM_LAUNCH(false, 4, kArgmaxCommit);
   } else {
@@ -530,6 +588,27 @@ int proj_splits(int M, int K, int Nout) {
   return best;
 }
 
+bool proj_swiglu_fused(int M, int K, int inter) {
+  return lmhead_mb(M) == 4 && proj_splits(M, K, 2 * inter) == 1;
+}
+
+hipError_t launch_proj_swiglu(const void* hidden, const void* w_gu_packed, void* act, int M,
+                              int K, int inter, hipStream_t stream) {
+  const int total = (2 * inter + kVT - 1) / kVT;  // one row block, one split
+  const bf16_t* h = static_cast<const bf16_t*>(hidden);
+  const bf16_t* wv = static_cast<const bf16_t*>(w_gu_packed);
+  bf16_t* a = static_cast<bf16_t*>(act);
+  if (proj_ring(M, K) == 4)
+    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kSwiGLU, 2, 4>), dim3(total), dim3(kThreads),
+                       0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M, K, 2 * inter, 1,
+                       total, nullptr, 1, a, inter);
+  else
+    hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kSwiGLU, 2, 2>), dim3(total), dim3(kThreads),
+                       0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M, K, 2 * inter, 1,
+                       total, nullptr, 1, a, inter);
+  return hipGetLastError();
+}
+
 hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, int M, int K,
                        int Nout, int nsplit, hipStream_t stream) {
   const int mb = lmhead_mb(M);
@@ -541,15 +620,15 @@ hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, in
   if (mb == 4 && proj_ring(M, K) == 4)
     hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 2, 4>), dim3(total),
                        dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
-                       K, Nout, nmt, total, part, nsplit);
+                       K, Nout, nmt, total, part, nsplit, nullptr, 0);
   else if (mb == 4)
     hipLaunchKernelGGL((lmhead_bf16_kernel<true, 4, kStorePartial, 2, 2>), dim3(total),
                        dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
-                       K, Nout, nmt, total, part, nsplit);
+                       K, Nout, nmt, total, part, nsplit, nullptr, 0);
   else
     hipLaunchKernelGGL((lmhead_bf16_kernel<true, 8, kStorePartial, 2>), dim3(total),
                        dim3(kThreads), 0, stream, h, wv, nullptr, nullptr, nullptr, nullptr, M,
-                       K, Nout, nmt, total, part, nsplit);
+                       K, Nout, nmt, total, part, nsplit, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -242,8 +242,10 @@ __global__ __launch_bounds__(kNormThreads) void epi_resid_norm_kernel(
 // of 64, since hidden is a multiple of 256).
 int norm_threads(int hidden) { return hidden / 4 < kNormThreads ? hidden / 4 : kNormThreads; }
 
-// ---- after the gate/up projection (gate columns [0, I), up columns
-// [I, 2I)): a = bf16(silu(gate) * up), four columns per thread.
+// ---- after the gate/up projection when it runs split: a = bf16(silu(gate) *
+// up), four columns per thread.  The weight is packed interleaved, so the
+// gate value of feature f = 64 t + j is column 128 t + j of the partial sums
+// and its up value column 128 t + 64 + j.
 __global__ __launch_bounds__(256) void epi_swiglu_kernel(const float* __restrict__ part,
                                                          int nsplit, int M, int I,
                                                          bf16_t* __restrict__ a) {
@@ -253,11 +255,12 @@ __global__ __launch_bounds__(256) void epi_swiglu_kernel(const float* __restrict
        t += (size_t)gridDim.x * 256) {
     const int m = (int)(t / q4);
     const int j = (int)(t - (size_t)m * q4) * 4;
+    const int cg = 128 * (j >> 6) + (j & 63);
     f32x4_t g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nsplit; ++s) {
       const float* row = part + ((size_t)s * M + m) * (2 * (size_t)I);
-      g += *reinterpret_cast<const f32x4_t*>(row + j);
-      u += *reinterpret_cast<const f32x4_t*>(row + I + j);
+      g += *reinterpret_cast<const f32x4_t*>(row + cg);
+      u += *reinterpret_cast<const f32x4_t*>(row + cg + 64);
     }
     float o[4];
 #pragma unroll
@@ -288,8 +291,7 @@ PassPlan pass_plan(const tv_model_dims& d, int B, int N, int max_seq_len) {
   upd((size_t)p.s_o * d.hidden);
   upd((size_t)p.s_gu * 2 * d.inter);
   upd((size_t)p.s_down * d.hidden);
-  size_t gin = (size_t)d.hidden;
-  if ((size_t)d.inter > gin) gin = d.inter;
+  size_t gin = (size_t)d.hidden;  // normalised hidden rows or attention output
   if ((size_t)d.Hq * d.D > gin) gin = (size_t)d.Hq * d.D;
   size_t off = 0;
   p.off_lm = off;
@@ -302,6 +304,8 @@ PassPlan pass_plan(const tv_model_dims& d, int B, int N, int max_seq_len) {
   off += align256((size_t)M * gin * 2);
   p.off_q = off;
   off += align256((size_t)M * d.Hq * d.D * 2);
+  p.off_act = off;
+  off += align256((size_t)M * d.inter * 2);
   p.off_part = off;
   off += align256((size_t)M * part * 4);
   p.off_attn = off;
@@ -324,6 +328,8 @@ hipError_t launch_verify_pass(const tv_model_dims& d, const tv_model_weights& w,
   float* x = reinterpret_cast<float*>(base + p.off_x);
   bf16_t* gin = reinterpret_cast<bf16_t*>(base + p.off_gin);
   bf16_t* Q = reinterpret_cast<bf16_t*>(base + p.off_q);
+  bf16_t* act = reinterpret_cast<bf16_t*>(base + p.off_act);
+  const bool fused_mlp = proj_swiglu_fused(M, d.hidden, d.inter);
   float* part = reinterpret_cast<float*>(base + p.off_part);
   void* attn_ws = base + p.off_attn;
   const int qkv = (d.Hq + 2 * d.Hkv) * d.D;
@@ -368,14 +374,21 @@ hipError_t launch_verify_pass(const tv_model_dims& d, const tv_model_weights& w,
                        part, p.s_o, M, d.hidden, x, ln2 + (size_t)ly * d.hidden, gin, nullptr,
                        d.rms_eps);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_proj(gin, wgu + ly * pb_gu, part, M, d.hidden, 2 * d.inter, p.s_gu, stream)))
-      return e;
-    const size_t sw_items = (size_t)M * (d.inter / 4);
-    const unsigned sw_grid = (unsigned)((sw_items + 255) / 256 < 2048 ? (sw_items + 255) / 256 : 2048);
-    hipLaunchKernelGGL(epi_swiglu_kernel, dim3(sw_grid), dim3(256), 0, stream, part, p.s_gu, M,
-                       d.inter, gin);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if ((e = launch_proj(gin, wdown + ly * pb_down, part, M, d.inter, d.hidden, p.s_down,
+    if (fused_mlp) {
+      if ((e = launch_proj_swiglu(gin, wgu + ly * pb_gu, act, M, d.hidden, d.inter, stream)))
+        return e;
+    } else {
+      if ((e = launch_proj(gin, wgu + ly * pb_gu, part, M, d.hidden, 2 * d.inter, p.s_gu,
+                           stream)))
+        return e;
+      const size_t sw_items = (size_t)M * (d.inter / 4);
+      const unsigned sw_grid =
+          (unsigned)((sw_items + 255) / 256 < 2048 ? (sw_items + 255) / 256 : 2048);
+      hipLaunchKernelGGL(epi_swiglu_kernel, dim3(sw_grid), dim3(256), 0, stream, part, p.s_gu,
+                         M, d.inter, act);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = launch_proj(act, wdown + ly * pb_down, part, M, d.inter, d.hidden, p.s_down,
                          stream)))
       return e;
     const bool last = ly + 1 == d.layers;

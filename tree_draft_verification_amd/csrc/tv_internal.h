@@ -105,6 +105,10 @@ size_t lmhead_ws_bytes(int M, int K, int V, int dtype);
 size_t lmhead_packed_bytes(int V, int K);
 
 hipError_t launch_lmhead_pack(const void* w, void* packed, int V, int K, hipStream_t stream);
+// A gate/up weight [2 inter][K] packed with gate and up rows interleaved per
+// 128-row tile (64 gate rows, then the 64 up rows of the same features).
+hipError_t launch_pack_gate_up(const void* w, void* packed, int inter, int K,
+                               hipStream_t stream);
 
 // The first lmhead_zero_bytes(M) bytes of ws must be zero and are left zero.
 size_t lmhead_zero_bytes(int M);
@@ -137,6 +141,11 @@ hipError_t launch_gemm32_store(const void* hidden, const void* w_packed, float* 
 
 // Split count of a packed-weight projection out[M][Nout] = H[M][K] W^T.
 int proj_splits(int M, int K, int Nout);
+// The gate/up projection with silu(gate) * up in its epilogue (one row block
+// of M <= 64 rows whose split count is 1): a[M][inter] bf16.
+bool proj_swiglu_fused(int M, int K, int inter);
+hipError_t launch_proj_swiglu(const void* hidden, const void* w_gu_packed, void* act, int M,
+                              int K, int inter, hipStream_t stream);
 
 // fp32 partial sums part[nsplit][M][Nout] (W packed as by launch_lmhead_pack).
 hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, int M, int K,
@@ -147,7 +156,7 @@ hipError_t launch_proj(const void* hidden, const void* w_packed, float* part, in
 struct PassPlan {
   int s_qkv, s_o, s_gu, s_down;  // split-K factors of the four projections
   AttnPlan attn;
-  size_t off_lm, off_pos, off_x, off_gin, off_q, off_part, off_attn;  // workspace offsets
+  size_t off_lm, off_pos, off_x, off_gin, off_q, off_act, off_part, off_attn;  // workspace offsets
   size_t ws_bytes;
 };
 

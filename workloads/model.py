@@ -57,6 +57,11 @@ MODELS = {
     # so greedy choices are rarely near-ties: for multi-step decoding checks
     "loop_d128": ModelConfig("loop_d128", layers=3, hidden=512, Hq=8, Hkv=2, D=128,
                              inter=768, V=3000, lm_std=0.2, seed=2004),
+    # a wide MLP (128 gate/up tiles of 128 rows over a short k range), the
+    # shape at which the gate/up projection runs unsplit with silu(gate) * up
+    # in its own epilogue, as at Qwen3-8B scale
+    "wide_mlp": ModelConfig("wide_mlp", layers=2, hidden=256, Hq=2, Hkv=1, D=128, inter=8192,
+                            V=1000, seed=2005),
 }
 
 _W_KEYS = ("embed", "ln1", "w_qkv", "q_norm", "k_norm", "w_o", "ln2", "w_gu", "w_down",
