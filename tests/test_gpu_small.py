@@ -496,3 +496,68 @@ def test_compact_paged_hazard_rows_cross_pages():
     np.testing.assert_array_equal(to_host_bits(kp), k2)
     np.testing.assert_array_equal(to_host_bits(vp), v2)
     np.testing.assert_array_equal(sl.cpu().numpy(), lens2)
+
+
+# ---------------------------------------------------------------- graph replay
+
+def test_step_graph_replay_matches_eager():
+    """The four calls of a step captured once as a HIP graph (as bench.py times
+    them) replay bit for bit like the same calls launched one by one, on every
+    replay, with the caches and lengths restored in between by ordinary work."""
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = ATTN_CASES["q8_ragged3_N64"].replace(V=5000, hidden=512)
+    a = attn_inputs(wl)
+    lm = lmhead_inputs(wl)
+    tgt = oracle.lm_head_argmax(lm["hidden"], lm["w"], wl.dtype)["argmax"].reshape(wl.B, wl.N)
+    draft = i32_dev(draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt))
+    q = to_dev(a["q"], "bf16")
+    k0, v0 = to_dev(a["k_cache"], "bf16"), to_dev(a["v_cache"], "bf16")
+    k, v = k0.clone(), v0.clone()
+    lens0 = i32_dev(a["seq_lens"])
+    lens = lens0.clone()
+    par = i32_dev(a["parent"])
+    hid = to_dev(lm["hidden"], "bf16")
+    w = tv.tv_lmhead_pack_weights(to_dev(lm["w"], "bf16"))
+    msl = int(a["seq_lens"].max())
+    out = torch.empty_like(q)
+    arg = torch.empty(wl.B * wl.N, dtype=torch.int32, device="cuda")
+    P = 32
+    path = torch.empty((wl.B, P), dtype=torch.int32, device="cuda")
+    plen = torch.empty(wl.B, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(wl.B, dtype=torch.int32, device="cuda")
+    aws = torch.zeros(max(256, tv.tv_tree_verify_attn_workspace(wl.B, wl.N, wl.Hq, wl.Hkv, wl.D,
+                                                                msl, tv.TV_BF16)),
+                      dtype=torch.uint8, device="cuda")
+    lws = torch.zeros(tv.tv_lmhead_argmax_workspace(wl.B * wl.N, wl.hidden, wl.V, tv.TV_BF16),
+                      dtype=torch.uint8, device="cuda")
+
+    def step():
+        tv.tv_tree_verify_attn(q, k, v, lens, par, out, max_seq_len=msl, scale=a["scale"],
+                               workspace=aws)
+        tv.tv_lmhead_argmax(hid, w, arg, workspace=lws)
+        tv.tv_tree_accept(par, draft, arg, P, path=path, path_len=plen, bonus=bonus)
+        tv.tv_kv_compact(k, v, lens, path, plen)
+
+    def state():
+        return [t.clone() for t in (out, arg, path, plen, bonus, k, v, lens)]
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+        s.synchronize()
+        eager = state()
+        k.copy_(k0), v.copy_(v0), lens.copy_(lens0)
+        tv.tv_graph_begin(s)
+        step()
+        graph = tv.tv_graph_end(s)
+        for rep in range(3):
+            k.copy_(k0), v.copy_(v0), lens.copy_(lens0)
+            out.zero_(), arg.zero_(), plen.zero_()
+            graph.launch(s)
+            s.synchronize()
+            for i, (x, y) in enumerate(zip(state(), eager)):
+                assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                                   y.view(torch.int16) if y.dtype == torch.bfloat16 else y), \
+                    f"replay {rep}: output {i} differs from the eager step"
+    assert int(plen.min()) >= 1
