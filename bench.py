@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the tree-verification step on one MI355X.
 
-One step = tv_tree_verify_attn -> tv_lmhead_argmax -> tv_tree_accept ->
-tv_kv_compact on one stream, over one batch of synthetic inputs already
+One step = tv_tree_verify_attn -> tv_lmhead_argmax -> tv_accept_compact
+(acceptance and KV compaction in one launch; with --paged, tv_tree_accept ->
+tv_kv_compact_paged) on one stream, over one batch of synthetic inputs already
 resident in HBM (the Qwen3-8B-shaped layer with a 1024-token prefix and a
 64-node draft tree by default).  Prints one JSON line with verified tree
 nodes/s of the step captured once as a HIP graph and replayed, the step
@@ -72,7 +73,8 @@ def algorithmic_work(wl, a, path, path_len):
     compact_bytes = int(4 * moved * wl.Hkv * wl.D * e + 8 * wl.B)
     accept_bytes = int(12 * wl.B * wl.N + 4 * wl.B * (path.shape[1] + 2))
     return dict(attn=(attn_bytes, attn_flops), lmhead=(lm_bytes, lm_flops),
-                accept=(accept_bytes, 0), compact=(compact_bytes, 0))
+                accept=(accept_bytes, 0), compact=(compact_bytes, 0),
+                accept_compact=(accept_bytes + compact_bytes, 0))
 
 
 def roof_entry(nbytes, flops, us, dtype):
@@ -226,6 +228,9 @@ def main():
     draft = i32(draft_tokens(a["parent"], coins, argmax.cpu().numpy().reshape(wl.B, wl.N)))
     torch.cuda.synchronize()
 
+    # Contiguous caches: acceptance and compaction run as one launch
+    # (tv_accept_compact); paged caches use the two calls.
+    fused_tail = not ps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
           for _ in range(args.steps)]
 
@@ -244,13 +249,16 @@ def main():
         tv.tv_lmhead_argmax(hid, w_step, argmax, workspace=lm_ws)
         if events:
             events[2].record()
-        tv.tv_tree_accept(parent, draft, argmax, P, path=path, path_len=plen, bonus=bonus)
-        if events:
-            events[3].record()
-        if ps:
-            tv.tv_kv_compact_paged(kc, vc, block_table, lens, path, plen)
+        if fused_tail:
+            tv.tv_accept_compact(parent, draft, argmax, kc, vc, lens, P, path=path, path_len=plen,
+                                 bonus=bonus)
+            if events:
+                events[3].record()
         else:
-            tv.tv_kv_compact(kc, vc, lens, path, plen)
+            tv.tv_tree_accept(parent, draft, argmax, P, path=path, path_len=plen, bonus=bonus)
+            if events:
+                events[3].record()
+            tv.tv_kv_compact_paged(kc, vc, block_table, lens, path, plen)
         if events:
             events[4].record()
 
@@ -299,6 +307,10 @@ def main():
     names = ["attn", "lmhead", "accept", "compact"]
     per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            * 1e3 for j, n in enumerate(names)}
+    if fused_tail:  # one launch between events 2 and 4
+        per = {"attn": per["attn"], "lmhead": per["lmhead"],
+               "accept_compact": per["accept"] + per["compact"]}
+        names = ["attn", "lmhead", "accept_compact"]
     eager_us = float(np.mean([ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)])) * 1e3
     step_us = float(np.median(graph_per))
     wall_ms = (t1 - t0) * 1e3 / args.steps

@@ -226,6 +226,27 @@ int tv_kv_compact(void* k_cache, void* v_cache, int32_t* seq_lens,
                   int D, int Lcap, int P, int dtype, void* stream);
 
 /*
+ * Acceptance and compaction in one launch: exactly tv_tree_accept followed
+ * by tv_kv_compact on the same arguments (the same outputs, bit for bit),
+ * for the end of a verification step (JetSpec GitHub README, "JetSpec >
+ * Overview": the accepted path follows the target's own logits; EQSPEC/EXSPEC
+ * abstract, arXiv 2510.22876 on the RSS reader page: each sequence's KV state
+ * stays in step).  Arguments as for those two calls: parent, draft_tokens,
+ * target_tokens [B][N] int32; path [B][P], path_len [B], bonus [B] int32
+ * (written); k_cache, v_cache [B][Hkv][Lcap][D] dtype and seq_lens [B]
+ * (updated in place, seq_lens[b] += path_len[b]).  A sequence whose tree is
+ * malformed or whose path is longer than P gets path_len 0 and a status flag,
+ * and its cache and length are left as they are.
+ * Supported: N <= TV_MAX_NODES, P <= 64, D * sizeof(dtype) % 16 == 0.
+ */
+int tv_accept_compact(const int32_t* parent, const int32_t* draft_tokens,
+                      const int32_t* target_tokens, int32_t* path,
+                      int32_t* path_len, int32_t* bonus, void* k_cache,
+                      void* v_cache, int32_t* seq_lens, int B, int N, int P,
+                      int Hkv, int D, int Lcap, int dtype, int32_t* dev_status,
+                      void* stream);
+
+/*
  * KV compaction on paged caches (layout as for tv_tree_verify_attn_paged):
  * the same row moves as tv_kv_compact, through the block table; a move
  * whose page entry is outside the pool is skipped.  bf16 or fp32 pools,

@@ -40,6 +40,7 @@ def test_header_declares_the_four_calls():
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights", "tv_pack_gate_up_weights",
+              "tv_accept_compact",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
               "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
@@ -143,6 +144,23 @@ def test_accept_and_compact_host_validation(lib):
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 2048, 0, 0, None) == -1
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 4, 2048, 32, 0, None) == -2   # 8-byte rows
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 128, 2048, 32, 3, None) == -2
+    ac = lib.tv_accept_compact
+    # valid arguments apart from the one changed in each case (no call reaches the device)
+    args = [FAKE] * 9 + [2, 64, 32, 8, 128, 2048, 0, None, None]
+    bad = list(args); bad[0] = None
+    assert ac(*bad) == -1
+    bad = list(args); bad[8] = None
+    assert ac(*bad) == -1                       # seq_lens
+    bad = list(args); bad[10] = 0
+    assert ac(*bad) == -1                       # N
+    bad = list(args); bad[10] = 1025
+    assert ac(*bad) == -2                       # N > TV_MAX_NODES
+    bad = list(args); bad[11] = 65
+    assert ac(*bad) == -2                       # P > 64
+    bad = list(args); bad[13] = 4
+    assert ac(*bad) == -2                       # 8-byte rows
+    bad = list(args); bad[15] = 7
+    assert ac(*bad) == -2                       # dtype
 
 
 def _attn_paged(lib, **kw):
@@ -254,6 +272,7 @@ def test_binding_names_match_the_c_calls():
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
               "tv_tree_verify_attn_workspace", "tv_lmhead_argmax_workspace",
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights", "tv_pack_gate_up_weights",
+              "tv_accept_compact",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
               "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",

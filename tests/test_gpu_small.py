@@ -561,3 +561,37 @@ def test_step_graph_replay_matches_eager():
                                    y.view(torch.int16) if y.dtype == torch.bfloat16 else y), \
                     f"replay {rep}: output {i} differs from the eager step"
     assert int(plen.min()) >= 1
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "q8_ragged3_N64", "a3b_B2_L257_N200",
+                                  "g1_L64_N130"])
+def test_accept_compact_equals_the_two_calls(name):
+    """tv_accept_compact gives bit for bit what tv_tree_accept then
+    tv_kv_compact give, on workload trees with the GPU's own argmax as the
+    target and with planted bad trees and too-long paths."""
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = ATTN_CASES[name]
+    a = attn_inputs(wl)
+    rng = np.random.default_rng(wl.seed + 99)
+    tgt = rng.integers(0, 50, size=(wl.B, wl.N)).astype(np.int32)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt)
+    parent = a["parent"].copy()
+    if wl.B > 1:
+        parent[1, min(3, wl.N - 1)] = wl.N + 5 if wl.N > 3 else parent[1, 0]  # malformed tree
+    for P in (32, 2):  # 2: paths longer than P are rejected with a flag
+        ref_k, ref_v = to_dev(a["k_cache"], wl.dtype), to_dev(a["v_cache"], wl.dtype)
+        got_k, got_v = ref_k.clone(), ref_v.clone()
+        ref_l, got_l = i32_dev(a["seq_lens"]), i32_dev(a["seq_lens"])
+        st_ref = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+        st_got = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+        par, dr, tg = i32_dev(parent), i32_dev(draft), i32_dev(tgt)
+        p1, l1, b1 = tv.tv_tree_accept(par, dr, tg, P, dev_status=st_ref)
+        tv.tv_kv_compact(ref_k, ref_v, ref_l, p1, l1)
+        p2, l2, b2 = tv.tv_accept_compact(par, dr, tg, got_k, got_v, got_l, P, dev_status=st_got)
+        torch.cuda.synchronize()
+        for x, y in ((p1, p2), (l1, l2), (b1, b2), (ref_l, got_l), (st_ref, st_got)):
+            assert torch.equal(x, y), name
+        for x, y in ((ref_k, got_k), (ref_v, got_v)):  # caches bit for bit
+            assert np.array_equal(x.cpu().view(torch.int16 if wl.dtype == "bf16" else torch.int32),
+                                  y.cpu().view(torch.int16 if wl.dtype == "bf16" else torch.int32))

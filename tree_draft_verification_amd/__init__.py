@@ -40,7 +40,7 @@ __all__ = [
     "TreeVerifyError", "tv_tree_verify_attn", "tv_tree_verify_attn_workspace",
     "tv_lmhead_argmax", "tv_lmhead_argmax_workspace", "tv_lmhead_packed_bytes",
     "tv_lmhead_pack_weights", "tv_pack_gate_up_weights", "PackedWeights", "tv_tree_accept",
-    "tv_kv_compact", "tv_status_string", "tv_abi_version", "library_path",
+    "tv_kv_compact", "tv_accept_compact", "tv_status_string", "tv_abi_version", "library_path",
     "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace", "tv_kv_compact_paged",
     "Model", "tv_model_pack", "tv_verify_pass", "tv_verify_pass_workspace",
     "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "Graph", "tv_graph_begin",
@@ -322,6 +322,36 @@ def tv_kv_compact(k_cache, v_cache, seq_lens, path, path_len) -> None:
     st = _lib_handle().tv_kv_compact(_ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(path),
                             _ptr(path_len), B, Hkv, D, Lcap, P, dt, _stream(k_cache.device))
     _check("tv_kv_compact", st)
+
+
+def tv_accept_compact(parent, draft_tokens, target_tokens, k_cache, v_cache, seq_lens,
+                      P: int = 32, *, path=None, path_len=None, bonus=None, dev_status=None):
+    """tv_tree_accept then tv_kv_compact in one launch; returns (path, path_len, bonus)."""
+    B, N = parent.shape
+    _i32(parent, (B, N), "parent")
+    _i32(draft_tokens, (B, N), "draft_tokens")
+    target_tokens = target_tokens.reshape(B, N)
+    _i32(target_tokens, (B, N), "target_tokens")
+    Bk, Hkv, Lcap, D = k_cache.shape
+    if Bk != B or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache disagree with each other or with the batch")
+    _i32(seq_lens, (B,), "seq_lens")
+    dev = parent.device
+    if path is None:
+        path = torch.empty((B, P), dtype=torch.int32, device=dev)
+    if path_len is None:
+        path_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if bonus is None:
+        bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    _i32(path, (B, P), "path")
+    _i32(path_len, (B,), "path_len")
+    _i32(bonus, (B,), "bonus")
+    st = _lib_handle().tv_accept_compact(
+        _ptr(parent), _ptr(draft_tokens), _ptr(target_tokens), _ptr(path), _ptr(path_len),
+        _ptr(bonus), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), B, N, P, Hkv, D, Lcap,
+        _dtype_code(k_cache), _ptr(dev_status), _stream(dev))
+    _check("tv_accept_compact", st)
+    return path, path_len, bonus
 
 
 def tv_kv_compact_paged(k_pages, v_pages, block_table, seq_lens, path, path_len) -> None:

@@ -49,6 +49,8 @@ SIGNATURES = {
     "tv_pack_gate_up_weights": (_i, [_p, _p, _i, _i, _i, _p]),
     "tv_tree_accept": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _p, _p]),
     "tv_kv_compact": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
+    "tv_accept_compact": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                               _p, _p]),
     "tv_verify_pass_workspace": (_sz, [_pd, _i, _i, _i]),
     "tv_verify_pass": (_i, [_pd, _pw, _p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _p, _p, _sz,
                             _p, _p]),

@@ -193,6 +193,26 @@ int tv_kv_compact(void* k_cache, void* v_cache, int32_t* seq_lens, const int32_t
                                           Lcap, P, dtype, static_cast<hipStream_t>(stream)));
 }
 
+int tv_accept_compact(const int32_t* parent, const int32_t* draft_tokens,
+                      const int32_t* target_tokens, int32_t* path, int32_t* path_len,
+                      int32_t* bonus, void* k_cache, void* v_cache, int32_t* seq_lens, int B,
+                      int N, int P, int Hkv, int D, int Lcap, int dtype, int32_t* dev_status,
+                      void* stream) {
+  if (!parent || !draft_tokens || !target_tokens || !path || !path_len || !bonus || !k_cache ||
+      !v_cache || !seq_lens)
+    return TV_EINVAL;
+  if (B < 1 || N < 1 || P < 1 || Hkv < 1 || D < 1 || Lcap < 1) return TV_EINVAL;
+  if (!dtype_ok(dtype)) return TV_ENOTSUP;
+  const int esz = dtype == TV_F32 ? 4 : 2;
+  if (N > TV_MAX_NODES || P > 64 || (D * esz) % 16 || (long long)P * D * esz > 65536)
+    return TV_ENOTSUP;
+  if (B > 65535) return TV_ENOTSUP;
+  return hip_status(tv::launch_accept_compact(parent, draft_tokens, target_tokens, path, path_len,
+                                              bonus, k_cache, v_cache, seq_lens, B, N, P, Hkv, D,
+                                              Lcap, dtype, dev_status,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- multi-layer pass

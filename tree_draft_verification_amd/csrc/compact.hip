@@ -21,7 +21,15 @@
 // group of planes - in LDS, waits at a barrier and only then writes.  Rows
 // with path[j] == j are skipped.  Accesses are 16-byte vectors, consecutive
 // threads on consecutive 16-byte pieces of a row.
-#include "tv_internal.h"
+//
+// Fused with acceptance (ACCEPT): each workgroup first selects its sequence's
+// accepted path itself (accept_core.h; a few LDS rounds over the tree, so
+// the workgroups of one sequence need not wait for each other), workgroup 0
+// of the sequence writes path, path_len and bonus, and the moves use the
+// path from LDS: one launch instead of two.
+#include <type_traits>
+
+#include "accept_core.h"
 
 namespace tv {
 namespace {
@@ -32,6 +40,15 @@ constexpr int kStageBytes = 64 * 1024;  // LDS staging per workgroup
 struct PagedArgs {
   const int32_t* block_table;  // nullptr: contiguous planes
   int max_blocks, page_shift, num_pages;
+};
+
+struct AcceptArgs {  // inputs and outputs of the fused acceptance
+  const int32_t* parent;
+  const int32_t* draft;
+  const int32_t* target;
+  int32_t* bonus;
+  int32_t* dev_status;
+  int N;
 };
 
 // Byte offset of row `row` of plane (b, head) in a cache, or -1 when a
@@ -49,26 +66,41 @@ __device__ __forceinline__ long long row_offset(const PagedArgs& pa, int b, int 
   }
 }
 
-template <bool PAGED>
+template <bool PAGED, bool ACCEPT>
 __global__ __launch_bounds__(kThreads) void compact_kernel(
     char* __restrict__ kc, char* __restrict__ vc, int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ path, const int32_t* __restrict__ path_len, int Hkv, int Lcap,
+    int32_t* __restrict__ path, int32_t* __restrict__ path_len, int Hkv, int Lcap,
     int P, int row_bytes, PagedArgs pa, int layers, long long layer_bytes, int groups,
-    unsigned* __restrict__ counters) {
+    unsigned* __restrict__ counters, AcceptArgs ac) {
   __shared__ uint4 stage[kStageBytes / 16];
   __shared__ int16_t s_move[64];  // j of every row that moves
   __shared__ int s_nmove;
   __shared__ int s_last;
+  struct NoAccept {};
+  __shared__ std::conditional_t<ACCEPT, AcceptLds, NoAccept> s_acc;
   const int b = blockIdx.x / groups;
   const int grp = blockIdx.x - b * groups;
   const int tid = threadIdx.x;
   const int L = seq_lens[b];
-  int n = path_len[b];
-  n = n < 0 ? 0 : (n > P ? P : n);
+  int n;
+  const int* pth;
+  if constexpr (ACCEPT) {
+    // one wavefront selects the path (its LDS rounds need no workgroup
+    // barriers); the workgroup waits once for the result
+    const size_t r = (size_t)b * ac.N;
+    if (tid < 64) accept_sequence<64>(s_acc, ac.parent + r, ac.draft + r, ac.target + r, ac.N, P);
+    __syncthreads();
+    if (grp == 0) accept_write<kThreads>(s_acc, b, P, path, path_len, ac.bonus, ac.dev_status);
+    n = s_acc.res[0];
+    pth = s_acc.path;
+  } else {
+    n = path_len[b];
+    n = n < 0 ? 0 : (n > P ? P : n);
+    pth = path + (size_t)b * P;
+  }
   // caller contract broken: touch nothing (the length is left as it was);
   // every workgroup of the sequence takes this branch together
   if (L < 0 || L + n > Lcap) return;
-  const int32_t* pth = path + (size_t)b * P;
   if (tid == 0) {
     int m = 0;
     for (int j = 0; j < n; ++j) {
@@ -153,13 +185,15 @@ hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t*
   if (block_table != nullptr) {
     while ((1 << pa.page_shift) < page_size) ++pa.page_shift;
     Lcap = max_blocks << pa.page_shift;
-    hipLaunchKernelGGL(compact_kernel<true>, dim3(B), dim3(kThreads), 0, stream,
-                       static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len,
-                       Hkv, Lcap, P, row_bytes, pa, 1, 0LL, 1, nullptr);
+    hipLaunchKernelGGL((compact_kernel<true, false>), dim3(B), dim3(kThreads), 0, stream,
+                       static_cast<char*>(k), static_cast<char*>(v), seq_lens,
+                       const_cast<int32_t*>(path), const_cast<int32_t*>(path_len), Hkv, Lcap, P,
+                       row_bytes, pa, 1, 0LL, 1, nullptr, AcceptArgs{});
   } else {
-    hipLaunchKernelGGL(compact_kernel<false>, dim3(B), dim3(kThreads), 0, stream,
-                       static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len,
-                       Hkv, Lcap, P, row_bytes, pa, 1, 0LL, 1, nullptr);
+    hipLaunchKernelGGL((compact_kernel<false, false>), dim3(B), dim3(kThreads), 0, stream,
+                       static_cast<char*>(k), static_cast<char*>(v), seq_lens,
+                       const_cast<int32_t*>(path), const_cast<int32_t*>(path_len), Hkv, Lcap, P,
+                       row_bytes, pa, 1, 0LL, 1, nullptr, AcceptArgs{});
   }
   return hipGetLastError();
 }
@@ -178,9 +212,26 @@ hipError_t launch_kv_compact_layers(void* k, void* v, int32_t* seq_lens, const i
   if (groups > cap) groups = cap;
   if (groups < 1) groups = 1;
   PagedArgs pa{nullptr, 0, 0, 0};
-  hipLaunchKernelGGL(compact_kernel<false>, dim3(B * groups), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((compact_kernel<false, false>), dim3(B * groups), dim3(kThreads), 0, stream,
+                     static_cast<char*>(k), static_cast<char*>(v), seq_lens,
+                     const_cast<int32_t*>(path), const_cast<int32_t*>(path_len), Hkv, Lcap, P,
+                     row_bytes, pa, layers, layer_bytes, groups, counters, AcceptArgs{});
+  return hipGetLastError();
+}
+
+// Acceptance and the compaction of a single-layer contiguous cache in one
+// launch: one workgroup per sequence.
+hipError_t launch_accept_compact(const int32_t* parent, const int32_t* draft,
+                                 const int32_t* target, int32_t* path, int32_t* path_len,
+                                 int32_t* bonus, void* k, void* v, int32_t* seq_lens, int B,
+                                 int N, int P, int Hkv, int D, int Lcap, int dtype,
+                                 int32_t* dev_status, hipStream_t stream) {
+  const int row_bytes = D * (dtype == TV_F32 ? 4 : 2);
+  PagedArgs pa{nullptr, 0, 0, 0};
+  AcceptArgs ac{parent, draft, target, bonus, dev_status, N};
+  hipLaunchKernelGGL((compact_kernel<false, true>), dim3(B), dim3(kThreads), 0, stream,
                      static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len, Hkv,
-                     Lcap, P, row_bytes, pa, layers, layer_bytes, groups, counters);
+                     Lcap, P, row_bytes, pa, 1, 0LL, 1, nullptr, ac);
   return hipGetLastError();
 }
 

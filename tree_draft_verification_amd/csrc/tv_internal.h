@@ -126,6 +126,11 @@ hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t*
                              int Lcap, int P, int dtype, hipStream_t stream,
                              const int32_t* block_table = nullptr, int max_blocks = 0,
                              int page_size = 0, int num_pages = 0);
+hipError_t launch_accept_compact(const int32_t* parent, const int32_t* draft,
+                                 const int32_t* target, int32_t* path, int32_t* path_len,
+                                 int32_t* bonus, void* k, void* v, int32_t* seq_lens, int B,
+                                 int N, int P, int Hkv, int D, int Lcap, int dtype,
+                                 int32_t* dev_status, hipStream_t stream);
 
 // ---------------------------------------------------------------- products with M > 64 rows
 
