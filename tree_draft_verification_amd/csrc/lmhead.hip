@@ -98,15 +98,20 @@ enum : int {
 // of nsplit and writes its partial sums to part[ks][M][V]; an epilogue
 // kernel adds the splits in a fixed order, so the result is deterministic.
 //
+// MODE kSwiGLU is the gate/up projection of a layer's MLP over the whole k
+// range, with gate and up rows interleaved per tile (see pack_kernel): it
+// writes bf16 silu(gate) * up for the tile's 64 features.
+//
 // RING is the depth of the register ring of W chunks (loads in flight per
-// wavefront): 2 where several workgroups share a CU (the LM head), 4 for the
-// projections, which run about one workgroup per CU and need the deeper
-// pipeline to keep enough bytes in flight.
+// wavefront).  Every form uses 2: with several workgroups per CU (the LM
+// head) a deeper ring only costs occupancy, and for the projections (about
+// one workgroup per CU) a sweep of depth 2 and 4 found no gain from 4.
 //
 // HD is the depth of the H stage prefetch: 1 loads a chunk's H slice while
 // the previous chunk is multiplied; deeper rings keep HD chunks in flight
 // (projections: one workgroup per CU, so an H load's L2 latency is not
-// hidden by other workgroups).  A trip covers max(RING, HD) chunks.
+// hidden by other workgroups; 4 deep: 5 % on the multi-layer pass).  A trip
+// covers max(RING, HD) chunks.
 template <bool PACKED, int MB, int MODE, int RING = 2, int HD = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MB == 4 ? 2 : 1)))
 void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
