@@ -35,7 +35,8 @@
 //     tree tiles that no node of the block can see are skipped.
 //   * Long prefixes can be split across workgroups (split-KV): each writes
 //     fp32 (reference max, sum, unnormalised output) partials and a combine
-//     kernel merges them; the tree keys go to the last split.
+//     kernel merges them; the tree keys then get the last split to
+//     themselves.
 //   * Workgroup ids are remapped so that the blocks reading the same K/V rows
 //     run on the same die (shared L2).
 // fp32 kernel: a plain VALU kernel for small fp32 problems.
@@ -656,6 +657,15 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dt
       p.nsplit = (ntiles + per - 1) / per;
     }
   }
+  // With the prefix split, the tree keys get a split of their own (the last,
+  // whose prefix range is empty) while the grid stays within the target:
+  // otherwise the workgroup that owns the last prefix chunk also walks the
+  // parents, builds the ancestor words and runs the tree tiles, and sets the
+  // critical path (measured 10-13 % off the attention time at 512-2048-token
+  // prefixes; past the target, the extra workgroups form a second wave).
+  if (dtype == TV_BF16 && p.nsplit > 1 &&
+      (long)B * Hkv * p.nqblk * (p.nsplit + 1) <= want_blocks)
+    p.nsplit += 1;
   p.ws_bytes = 0;
   if (p.nsplit > 1) {
     const size_t rows = (size_t)B * Hkv * p.nqblk * p.rows * p.nsplit;
