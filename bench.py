@@ -13,7 +13,7 @@ steps), and the fp64 oracle timed on this host's cores as a CPU baseline.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--paged PAGE_SIZE] [--model qwen3_8b] [--tree CONFIG]
-                    [--decode STEPS --model qwen3_8b]
+                    [--decode STEPS --model qwen3_8b] [--compact-stack LAYERS]
 
 --paged keeps the key/value caches in pages of a shared pool (placed by a
 seeded random permutation) and runs the paged attention and compaction calls.
@@ -25,6 +25,12 @@ of draft-head log-probabilities (e.g. quickstart_d20_w7_n128).
 --decode runs STEPS steps of ragged speculative decoding with the model
 (tree construction, multi-layer pass, acceptance, compaction per step) and
 reports generated tokens per second of device time.
+--compact-stack times one tv_kv_compact_layers launch over LAYERS stacked
+layers of the ragged-batch geometry (8 sequences, 8 KV heads of 128, prefixes
+512-8192, 64-node trees of depth <= 12), each sequence accepting the root
+path of its deepest node, with L2 and the infinity cache evicted (by a
+1 GiB read) before each launch: the bandwidth evidence for compaction, whose
+single-layer launches are too small to say anything but latency.
 """
 from __future__ import annotations
 
@@ -48,6 +54,8 @@ DEFAULT_WORKLOAD = "qwen3_8b_L1024_N64"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 LMHEAD_SOURCES = [os.path.join(ROOT, "tree_draft_verification_amd", "csrc", f)
                   for f in ("lmhead.hip", "tv_internal.h")]
+COMPACT_SOURCES = [os.path.join(ROOT, "tree_draft_verification_amd", "csrc", f)
+                   for f in ("compact.hip", "accept_core.h", "tv_internal.h")]
 
 
 def kernel_source_digest(paths) -> str:
@@ -151,6 +159,8 @@ def main():
     ap.add_argument("--tree-budget", type=int, default=63)
     ap.add_argument("--tree", default=None,
                     help="time draft-tree construction on this configuration")
+    ap.add_argument("--compact-stack", type=int, default=0,
+                    help="time layered KV compaction over this many stacked layers")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many bytes")
     args = ap.parse_args()
@@ -169,6 +179,9 @@ def main():
         return
     if args.tree:
         tree_bench(args)
+        return
+    if args.compact_stack:
+        compact_stack_bench(args)
         return
 
     import torch
@@ -602,6 +615,141 @@ def tree_bench(args):
         res["cpu_baseline"] = dict(value=round(cfg.B * reps / spent, 3), unit="trees/s",
                                    cores=int(cores), kind="oracle",
                                    sample=f"{reps} full build(s) of {cfg.name} ({spent:.1f} s)")
+    print(json.dumps(res), flush=True)
+
+
+def compact_stack_bench(args):
+    """One tv_kv_compact_layers launch over many stacked layers."""
+    import torch
+
+    import tree_draft_verification_amd as tv
+    from workloads import WORKLOADS, attn_inputs
+
+    t_setup = time.perf_counter()
+
+    def progress(msg):
+        print(f"[bench] {time.perf_counter() - t_setup:6.1f} s  {msg}", file=sys.stderr, flush=True)
+
+    wl = WORKLOADS["qwen3_8b_ragged8_N64"]
+    layers = args.compact_stack
+    a = attn_inputs(wl.replace(Hq=wl.Hkv, D=8))  # trees and prefix lengths only
+    par, depth, lens_h = a["parent"], a["depth"], a["seq_lens"]
+    B, Hkv, D, Lcap, P = wl.B, wl.Hkv, wl.D, wl.Lcap, 32
+    path_h = np.full((B, P), -1, dtype=np.int32)
+    plen_h = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        node = int(np.argmax(depth[b]))         # deepest node, smallest index
+        chain = []
+        while node >= 0:
+            chain.append(node)
+            node = int(par[b, node])
+        chain.reverse()
+        path_h[b, :len(chain)] = chain
+        plen_h[b] = len(chain)
+    moved = int(sum((path_h[b, :plen_h[b]] != np.arange(plen_h[b])).sum() for b in range(B)))
+    e = 2
+    nbytes = 4 * moved * Hkv * D * e * layers + 8 * B
+    dev = torch.device("cuda:0")
+    plane = (layers, B, Hkv, Lcap, D)
+    progress(f"stacked caches: {layers} layers, "
+             f"{2 * np.prod(plane) * e / 2**30:.1f} GiB")
+    k = torch.empty(plane, dtype=torch.int16, device=dev)
+    v = torch.empty(plane, dtype=torch.int16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed)
+    for b in range(B):   # only the tree rows are read; fill them with seeded bits
+        L = int(lens_h[b])
+        for c in (k, v):
+            c[:, b, :, L:L + wl.N].random_(-32768, 32767, generator=g)
+    lens0 = torch.from_numpy(lens_h.astype(np.int32)).to(dev)
+    lens = lens0.clone()
+    path = torch.from_numpy(path_h).to(dev)
+    plen = torch.from_numpy(plen_h).to(dev)
+    ws = torch.zeros(tv.tv_kv_compact_layers_workspace(B), dtype=torch.uint8, device=dev)
+    # Cold caches: a 1 GiB read before each launch evicts L2 and the 256 MB
+    # infinity cache.  A read leaves no dirty lines behind; a write-based
+    # flush would leave write-backs that compete with the timed kernel.
+    flush = torch.zeros(1 << 27, dtype=torch.int64, device=dev)
+    flush_out = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def evict():
+        torch.sum(flush, dim=0, out=flush_out)
+
+    kb, vb = k.view(torch.bfloat16), v.view(torch.bfloat16)
+
+    # one launch checked against the moves done by indexing (bits)
+    src = [torch.from_numpy(int(lens_h[b]) + path_h[b, :plen_h[b]].astype(np.int64)).to(dev)
+           for b in range(B)]
+    want_k = [k[:, b, :, src[b]].clone() for b in range(B)]
+    want_v = [v[:, b, :, src[b]].clone() for b in range(B)]
+    tv.tv_kv_compact_layers(kb, vb, lens, path, plen, workspace=ws)
+    torch.cuda.synchronize()
+    for b in range(B):
+        L, n = int(lens_h[b]), int(plen_h[b])
+        if not (torch.equal(k[:, b, :, L:L + n], want_k[b])
+                and torch.equal(v[:, b, :, L:L + n], want_v[b])):
+            raise SystemExit(f"bench.py: stacked compaction moved the wrong rows (sequence {b})")
+    if not torch.equal(lens.cpu(), lens0.cpu() + plen.cpu()):
+        raise SystemExit("bench.py: stacked compaction left wrong lengths")
+    del want_k, want_v
+    progress("stacked compaction checked")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        lens.copy_(lens0)
+        evict()
+        if i >= args.warmup:
+            ev[i - args.warmup][0].record()
+        tv.tv_kv_compact_layers(kb, vb, lens, path, plen, workspace=ws)
+        if i >= args.warmup:
+            ev[i - args.warmup][1].record()
+    torch.cuda.synchronize()
+    per = np.array([x[0].elapsed_time(x[1]) * 1e3 for x in ev])
+    us = float(np.median(per))
+    achieved = nbytes / (us * 1e-6) / 1e9
+    # context: a plain device copy with the same bytes read and written,
+    # timed the same way (cold, between events)
+    half = nbytes // 2
+    src_c = torch.empty(half, dtype=torch.uint8, device=dev)
+    dst_c = torch.empty_like(src_c)
+    evc = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        evict()
+        if i >= args.warmup:
+            evc[i - args.warmup][0].record()
+        dst_c.copy_(src_c)
+        if i >= args.warmup:
+            evc[i - args.warmup][1].record()
+    torch.cuda.synchronize()
+    copy_us = float(np.median([x[0].elapsed_time(x[1]) * 1e3 for x in evc]))
+    workload = f"{wl.name} geometry, {layers} stacked layers"
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            cnt = json.load(f).get("compact_kernel_layered", {})
+        if (cnt.get("workload") == workload
+                and cnt.get("source_digest") == kernel_source_digest(COMPACT_SOURCES)):
+            traffic = cnt.get("traffic_bytes")
+    res = {
+        "metric": "KV compaction bandwidth (tv_kv_compact_layers, one launch over stacked layers)",
+        "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (bits)",
+        "data": "synthetic (seeded trees and cache bits; cold caches)",
+        "config": {"workload": workload,
+                   "batch": B, "kv_heads": Hkv, "head_dim": D, "Lcap": Lcap,
+                   "layers": layers, "moved_rows_per_layer": moved,
+                   "path_lens": [int(x) for x in plen_h]},
+        "step_us": round(us, 2),
+        "step_us_p10_p90": [round(float(np.percentile(per, 10)), 2),
+                            round(float(np.percentile(per, 90)), 2)],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "compact_kernel<false, false> (layered)",
+                     "algorithmic_bytes": nbytes, "launch_us": round(us, 2)},
+        "plain_copy_same_bytes": {"us": round(copy_us, 2),
+                                  "gbs": round(nbytes / (copy_us * 1e-6) / 1e9, 1)},
+    }
     print(json.dumps(res), flush=True)
 
 

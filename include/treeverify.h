@@ -343,6 +343,8 @@ int tv_verify_pass(const tv_model_dims* dims, const tv_model_weights* weights,
  * planes; the last of them to finish updates the length through a counter in
  * `workspace` (tv_kv_compact_layers_workspace() bytes, zero-filled before
  * its first use and left zero by every call).
+ * Supported: as tv_kv_compact, with B <= 65535 and
+ * layers * (2 * Hkv)^2 < 2^32.
  */
 size_t tv_kv_compact_layers_workspace(int B);
 int tv_kv_compact_layers(void* k_cache, void* v_cache, int32_t* seq_lens,

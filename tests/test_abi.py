@@ -237,6 +237,8 @@ def test_pass_host_validation(lib):
     assert c(None, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 36, 0, FAKE, cw, None) == -1
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 0, 0, FAKE, cw, None) == -1
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 65, 36, 0, FAKE, cw, None) == -2
+    # plane indexing: layers * (2 Hkv)^2 must stay below 2^32
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 64, 128, 2048, 32, 262144, 0, FAKE, cw, None) == -2
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 36, 0, None, cw, None) == -3
     assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 8, 128, 2048, 32, 36, 0, FAKE, cw - 1, None) == -3
     # graphs: the null stream cannot be captured; null handles are rejected

@@ -287,7 +287,8 @@ int tv_kv_compact_layers(void* k_cache, void* v_cache, int32_t* seq_lens, const 
   if (!dtype_ok(dtype)) return TV_ENOTSUP;
   const int esz = dtype == TV_F32 ? 4 : 2;
   if ((D * esz) % 16 || P > 64 || (long long)P * D * esz > 65536) return TV_ENOTSUP;
-  if (B > 65535 || (long long)layers * 2 * Hkv > 2147483647LL) return TV_ENOTSUP;
+  // planes (layer, K|V, head) are indexed in 32 bits with quotients by 2 * Hkv
+  if (B > 65535 || (long long)layers * 4 * Hkv * Hkv >= 4294967296LL) return TV_ENOTSUP;
   if (!workspace || ws_bytes < tv_kv_compact_layers_workspace(B)) return TV_EWORKSPACE;
   return hip_status(tv::launch_kv_compact_layers(k_cache, v_cache, seq_lens, path, path_len, B,
                                                  Hkv, D, Lcap, P, layers, dtype,

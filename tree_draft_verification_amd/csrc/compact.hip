@@ -16,11 +16,15 @@
 // [Lcap][row]), the planes of all layers are shared out among several
 // workgroups per sequence; the last to finish updates the length.
 //
-// In-place hazard: move j reads row L+path[j], which move j' < j may be
-// writing when path[j] == j'; the hazard exists only inside a plane.  The workgroup therefore stages whole planes - all moved rows of a
-// group of planes - in LDS, waits at a barrier and only then writes.  Rows
-// with path[j] == j are skipped.  Accesses are 16-byte vectors, consecutive
-// threads on consecutive 16-byte pieces of a row.
+// In-place hazard: the row a move reads can be another move's destination
+// (path[j] == j' for a moved j'), only inside a plane.  An accepted path is
+// increasing with path[j] >= j, so the serial order in increasing j reads
+// every such row before overwriting it; the workgroup does the same by
+// loading all moved rows of whole planes into registers (at most 64 KB per
+// round), waiting at a barrier and only then writing.  Rows with
+// path[j] == j are skipped.  Accesses are 16-byte vectors, consecutive
+// threads on consecutive 16-byte pieces of a row, a thread's pieces of a
+// round all in flight together.
 //
 // Fused with acceptance (ACCEPT): each workgroup first selects its sequence's
 // accepted path itself (accept_core.h; a few LDS rounds over the tree, so
@@ -35,7 +39,10 @@ namespace tv {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kStageBytes = 64 * 1024;  // LDS staging per workgroup
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
+// (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kPer = 4;  // 16-byte pieces a thread holds per round (64 KB a workgroup)
 
 struct PagedArgs {
   const int32_t* block_table;  // nullptr: contiguous planes
@@ -51,29 +58,41 @@ struct AcceptArgs {  // inputs and outputs of the fused acceptance
   int N;
 };
 
-// Byte offset of row `row` of plane (b, head) in a cache, or -1 when a
-// paged entry is outside the pool.
+// n / d for n * d < 2^32: one multiply-high by m = ceil(2^32 / d)
+struct FastDiv {
+  unsigned d, m;
+};
+__device__ __forceinline__ FastDiv make_fastdiv(unsigned d) {
+  return {d, d == 1u ? 0u : 0xffffffffu / d + 1u};
+}
+__device__ __forceinline__ unsigned fast_div(unsigned n, FastDiv f) {
+  return f.d == 1u ? n : __umulhi(n, f.m);
+}
+
+// Byte offset of row `row` of sequence b in KV head 0 of a cache plane set
+// (head h adds h * head_stride), or -1 when a paged entry is outside the
+// pool.
 template <bool PAGED>
-__device__ __forceinline__ long long row_offset(const PagedArgs& pa, int b, int head, int Hkv,
-                                                int Lcap, int row, int row_bytes) {
+__device__ __forceinline__ long long row_part(const PagedArgs& pa, int b, int Hkv, int Lcap,
+                                              int row, int row_bytes) {
   if constexpr (PAGED) {
     const int pg = pa.block_table[(size_t)b * pa.max_blocks + (row >> pa.page_shift)];
     if (pg < 0 || pg >= pa.num_pages) return -1;
-    return ((((long long)pg * Hkv + head) << pa.page_shift) + (row & ((1 << pa.page_shift) - 1))) *
+    return (((long long)pg * Hkv << pa.page_shift) + (row & ((1 << pa.page_shift) - 1))) *
            row_bytes;
   } else {
-    return (((long long)b * Hkv + head) * Lcap + row) * row_bytes;
+    return ((long long)b * Hkv * Lcap + row) * row_bytes;
   }
 }
 
 template <bool PAGED, bool ACCEPT>
-__global__ __launch_bounds__(kThreads) void compact_kernel(
+__global__ __launch_bounds__(kThreads, (PAGED || ACCEPT) ? 4 : 8) void compact_kernel(
     char* __restrict__ kc, char* __restrict__ vc, int32_t* __restrict__ seq_lens,
     int32_t* __restrict__ path, int32_t* __restrict__ path_len, int Hkv, int Lcap,
     int P, int row_bytes, PagedArgs pa, int layers, long long layer_bytes, int groups,
     unsigned* __restrict__ counters, AcceptArgs ac) {
-  __shared__ uint4 stage[kStageBytes / 16];
-  __shared__ int16_t s_move[64];  // j of every row that moves
+  __shared__ long long s_src[64];  // row parts (head 0) of every move's source
+  __shared__ long long s_dst[64];  // and destination, in increasing j
   __shared__ int s_nmove;
   __shared__ int s_last;
   struct NoAccept {};
@@ -83,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
   const int tid = threadIdx.x;
   const int L = seq_lens[b];
   int n;
-  const int* pth;
+  int src = -1;  // path entry of lane tid (wavefront 0)
   if constexpr (ACCEPT) {
     // one wavefront selects the path (its LDS rounds need no workgroup
     // barriers); the workgroup waits once for the result
@@ -92,67 +111,82 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
     __syncthreads();
     if (grp == 0) accept_write<kThreads>(s_acc, b, P, path, path_len, ac.bonus, ac.dev_status);
     n = s_acc.res[0];
-    pth = s_acc.path;
+    if (tid < n) src = s_acc.path[tid];
   } else {
+    // the path is read together with the lengths (P <= 64 entries)
+    if (tid < P) src = path[(size_t)b * P + tid];
     n = path_len[b];
     n = n < 0 ? 0 : (n > P ? P : n);
-    pth = path + (size_t)b * P;
   }
   // caller contract broken: touch nothing (the length is left as it was);
   // every workgroup of the sequence takes this branch together
   if (L < 0 || L + n > Lcap) return;
-  if (tid == 0) {
-    int m = 0;
-    for (int j = 0; j < n; ++j) {
-      const int src = pth[j];
-      if (src != j && src >= 0 && L + src < Lcap) s_move[m++] = (int16_t)j;
+  // The rows that move, in increasing j: wavefront 0 locates both rows of
+  // every move (a paged move whose source or destination page is outside
+  // the pool is dropped) and ranks the moves with a ballot.
+  if (tid < 64) {
+    bool mv = tid < n && src != tid && src >= 0 && L + src < Lcap;
+    long long ps = 0, pd = 0;
+    if (mv) {
+      ps = row_part<PAGED>(pa, b, Hkv, Lcap, L + src, row_bytes);
+      pd = row_part<PAGED>(pa, b, Hkv, Lcap, L + tid, row_bytes);
+      mv = ps >= 0 && pd >= 0;
     }
-    s_nmove = m;
+    const unsigned long long bal = __ballot(mv);
+    if (mv) {
+      const int pos = __popcll(bal & ((1ull << tid) - 1ull));
+      s_src[pos] = ps;
+      s_dst[pos] = pd;
+    }
+    if (tid == 0) s_nmove = __popcll(bal);
   }
   __syncthreads();
   const int m = s_nmove;
   const int chunks = row_bytes / 16;
-  const int per_plane = m * chunks;  // staged pieces per plane
+  const int per_plane = m * chunks;  // pieces per plane
+  const long long head_stride =
+      PAGED ? (long long)row_bytes << pa.page_shift : (long long)Lcap * row_bytes;
   // planes (layer, K|V, head) of all layers, shared out among the groups
   const int planes_all = 2 * Hkv * layers;
   const int pb = (int)((long long)grp * planes_all / groups);
   const int pe = (int)((long long)(grp + 1) * planes_all / groups);
-  auto plane_base = [&](int p, int& h) -> char* {
-    const int ly = p / (2 * Hkv);
-    const int q = p - ly * 2 * Hkv;
-    h = q < Hkv ? q : q - Hkv;
-    return (q < Hkv ? kc : vc) + (long long)ly * layer_bytes;
-  };
   if (per_plane > 0) {
-    const int group = (kStageBytes / 16) / per_plane;  // >= 1: P * row_bytes <= 64 KB
+    // a round takes whole planes, at most kPer pieces per thread; the
+    // quotients below stay exact (pieces < 2^12 per round, and the host
+    // bounds planes_all * 2 * Hkv below 2^32)
+    const int group = kPer * kThreads / per_plane;  // >= 1: P * row_bytes <= 64 KB
+    const FastDiv div_pp = make_fastdiv(per_plane);
+    const FastDiv div_ch = make_fastdiv(chunks);
+    const FastDiv div_kv = make_fastdiv(2 * Hkv);
     for (int p0 = pb; p0 < pe; p0 += group) {
-      const int pn = min(group, pe - p0);
-      const int items = pn * per_plane;
-      for (int it = tid; it < items; it += kThreads) {
-        const int p = p0 + it / per_plane;
-        const int rem = it - (it / per_plane) * per_plane;
-        const int k = rem / chunks;
+      const int items = min(group, pe - p0) * per_plane;
+      u32x4_t val[kPer];
+      char* dst[kPer];
+      // straight-line loads, all in flight together (a thread past the end
+      // reloads the last piece and writes nothing)
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int it = min(tid + q * kThreads, items - 1);
+        const int pl = (int)fast_div(it, div_pp);
+        const int rem = it - pl * per_plane;
+        const int k = (int)fast_div(rem, div_ch);
         const int x = rem - k * chunks;
-        const int j = s_move[k];
-        int h;
-        const char* base = plane_base(p, h);
-        const long long off = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + pth[j], row_bytes);
-        if (off >= 0) stage[it] = reinterpret_cast<const uint4*>(base + off)[x];
+        const int p = p0 + pl;
+        const int ly = (int)fast_div(p, div_kv);
+        const int qh = p - ly * 2 * Hkv;
+        const int h = qh < Hkv ? qh : qh - Hkv;
+        char* base = (qh < Hkv ? kc : vc) + ly * layer_bytes + h * head_stride + 16 * x;
+        val[q] = *reinterpret_cast<const u32x4_t*>(base + s_src[k]);
+        dst[q] = tid + q * kThreads < items ? base + s_dst[k] : nullptr;
       }
+      // every read of these planes has returned before any write: each
+      // thread waits for its own loads, then the barrier; the next round's
+      // planes are others, so no barrier follows the writes
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       __syncthreads();
-      for (int it = tid; it < items; it += kThreads) {
-        const int p = p0 + it / per_plane;
-        const int rem = it - (it / per_plane) * per_plane;
-        const int k = rem / chunks;
-        const int x = rem - k * chunks;
-        const int j = s_move[k];
-        int h;
-        char* base = plane_base(p, h);
-        const long long src = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + pth[j], row_bytes);
-        const long long off = row_offset<PAGED>(pa, b, h, Hkv, Lcap, L + j, row_bytes);
-        if (off >= 0 && src >= 0) reinterpret_cast<uint4*>(base + off)[x] = stage[it];
-      }
-      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (dst[q] != nullptr) *reinterpret_cast<u32x4_t*>(dst[q]) = val[q];
     }
   }
   // The new length: every workgroup of the sequence has read L (before its
@@ -198,8 +232,9 @@ hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t*
   return hipGetLastError();
 }
 
-// Every layer in one launch: about eight planes per workgroup, at most 1024
-// workgroups in all.
+// Every layer in one launch: about eight planes per workgroup, at most 512
+// workgroups in all (two 1024-thread workgroups fit a compute unit, so the
+// grid is resident at once on 256 units and no workgroup waits for a slot).
 hipError_t launch_kv_compact_layers(void* k, void* v, int32_t* seq_lens, const int32_t* path,
                                     const int32_t* path_len, int B, int Hkv, int D, int Lcap,
                                     int P, int layers, int dtype, unsigned* counters,
@@ -208,7 +243,7 @@ hipError_t launch_kv_compact_layers(void* k, void* v, int32_t* seq_lens, const i
   const long long layer_bytes = (long long)B * Hkv * Lcap * row_bytes;
   const int planes = 2 * Hkv * layers;
   int groups = (planes + 7) / 8;
-  const int cap = 1024 / B > 1 ? 1024 / B : 1;
+  const int cap = 512 / B > 1 ? 512 / B : 1;
   if (groups > cap) groups = cap;
   if (groups < 1) groups = 1;
   PagedArgs pa{nullptr, 0, 0, 0};
