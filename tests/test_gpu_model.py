@@ -30,6 +30,12 @@ CASES = {
         B=3, Hq=8, Hkv=2, N=40, L_lo=10, L_hi=200, seed=62)),
     # unsplit gate/up projection with the fused silu(gate) * up epilogue
     "wide_mlp_N64_L200": ("wide_mlp", Q8.replace(Hq=2, Hkv=1, L_lo=200, L_hi=200, seed=63)),
+    # 512 and 640 rows: the products with 256-row H tiles (the last slice of
+    # 640 rows half empty)
+    "small_d128_B8_N64_M512": ("small_d128", WORKLOADS["qwen3_8b_ragged8_N64"].replace(
+        B=8, Hq=8, Hkv=2, N=64, L_lo=10, L_hi=120, seed=64)),
+    "small_d128_B10_N64_M640": ("small_d128", WORKLOADS["qwen3_8b_ragged8_N64"].replace(
+        B=10, Hq=8, Hkv=2, N=64, L_lo=10, L_hi=90, seed=65)),
 }
 
 
