@@ -31,6 +31,12 @@ ATTN_CASES = {
     "empty_prefix_N20": Q8.replace(L_lo=0, L_hi=0, N=20, seed=18),
     "single_node_L77": Q8.replace(L_lo=77, L_hi=77, N=1, seed=19),
     "f32_gqa_L90_N20": Q8.replace(dtype="f32", Hq=8, Hkv=2, L_lo=90, L_hi=90, N=20, seed=20),
+    # prefixes of 32 tiles and more: 128-row query blocks, K loaded straight
+    # into LDS, split prefixes with a ragged last tile
+    "q8_L2100_N64": Q8.replace(L_lo=2100, L_hi=2100, seed=21),
+    "q8_ragged2_L2000_3100_N64": WORKLOADS["qwen3_8b_ragged8_N64"].replace(
+        B=2, L_lo=2000, L_hi=3100, seed=22),
+    "q8_bfs_L2049_N256": WORKLOADS["qwen3_8b_L16384_N256"].replace(L_lo=2049, L_hi=2049, seed=23),
 }
 
 
@@ -391,6 +397,7 @@ PAGED_CASES = {
     "d64_bf16_L129_N33_ps32": ("d64_bf16_L129_N33", 32),
     "empty_prefix_N20_ps16": ("empty_prefix_N20", 16),
     "g1_L64_N130_ps128": ("g1_L64_N130", 128),
+    "q8_ragged2_L2000_3100_N64_ps16": ("q8_ragged2_L2000_3100_N64", 16),
 }
 
 
