@@ -19,11 +19,11 @@
 //     HBM once per die and the slices' rows stay in its L2.
 // What bounds it is the rate at which a compute unit's vector memory path
 // brings chunks in from L2 (about 74 cache lines in flight per CU, ~500
-// cycles each): the 256-row H tile halves the H bytes per product and runs
-// 11-14 % faster from 512 rows on; at 256 rows it would leave most CUs with
-// two tiles against three, so the 128-row tile stays there.  The 256-row
-// tile has no registers left for staging H, so H goes straight from memory
-// into LDS.
+// cycles each).  For the LM head from 512 rows on, a 256-row H tile halves
+// the H bytes per product and runs 6-14 % faster; it has no registers left
+// for staging H, so H goes straight from memory into LDS.  At 256 rows it
+// would leave most CUs with two tiles against three, and the split-K
+// projections would need twice the splits, so both keep the 128-row tile.
 // Operand lane layout of the 32 x 32 x 16 form (measured): lane l holds
 // row (or column) l % 32 and k values 8*(l/32) .. 8*(l/32)+7; result
 // register i of lane l is row 8*(i/4) + 4*(l/32) + i%4, column l % 32.
@@ -389,15 +389,19 @@ void gemm32w_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
   epilogue<MODE, MT>(acc, tl, s_key, keys, logits, part, M, V);
 }
 
+// The 256-row tile serves the LM head (one pass over k, argmax epilogue).
+// The split-K projections stay on 128-row tiles: with half as many tiles
+// they would take twice the splits, each with half the k range and twice
+// the partial sums, and measured slower (a 36-layer pass at 512 rows: 13.4
+// against 11.2 ms of projections).
 bool use_wide(int M) { return M >= kWideRows; }
-int h_rows(int M) { return use_wide(M) ? 256 : 128; }
 
 }  // namespace
 
 int gemm32_vtiles(int V) { return (V + kWT - 1) / kWT; }
 
 int gemm32_splits(int M, int K, int Nout) {
-  const int tiles = ((M + h_rows(M) - 1) / h_rows(M)) * gemm32_vtiles(Nout);
+  const int tiles = ((M + 127) / 128) * gemm32_vtiles(Nout);
   const int npair = K / (2 * kKC);
   int best = 1;
   for (int s = 1; s <= npair; ++s)  // about two workgroups per CU at most
@@ -408,7 +412,8 @@ int gemm32_splits(int M, int K, int Nout) {
 hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
                                 unsigned long long* keys, float* logits, int M, int K, int V,
                                 hipStream_t stream) {
-  const int nmt = (M + h_rows(M) - 1) / h_rows(M);
+  const int rows = use_wide(M) ? 256 : 128;
+  const int nmt = (M + rows - 1) / rows;
   const int total = nmt * gemm32_vtiles(V);
   const bf16_t* h = static_cast<const bf16_t*>(hidden);
   const bf16_t* w = static_cast<const bf16_t*>(w_packed);
@@ -423,16 +428,11 @@ hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
 
 hipError_t launch_gemm32_store(const void* hidden, const void* w_packed, float* part, int M,
                                int K, int Nout, int nsplit, hipStream_t stream) {
-  const int nmt = (M + h_rows(M) - 1) / h_rows(M);
+  const int nmt = (M + 127) / 128;
   const int total = nmt * gemm32_vtiles(Nout) * nsplit;
-  const bf16_t* h = static_cast<const bf16_t*>(hidden);
-  const bf16_t* w = static_cast<const bf16_t*>(w_packed);
-  if (use_wide(M))
-    hipLaunchKernelGGL(gemm32w_kernel<kGemmStore>, dim3(total), dim3(kThreads), 0, stream, h, w,
-                       nullptr, nullptr, part, M, K, Nout, nmt, nsplit, total);
-  else
-    hipLaunchKernelGGL(gemm32_kernel<kGemmStore>, dim3(total), dim3(kThreads), 0, stream, h, w,
-                       nullptr, nullptr, part, M, K, Nout, nmt, nsplit, total);
+  hipLaunchKernelGGL(gemm32_kernel<kGemmStore>, dim3(total), dim3(kThreads), 0, stream,
+                     static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed),
+                     nullptr, nullptr, part, M, K, Nout, nmt, nsplit, total);
   return hipGetLastError();
 }
 
