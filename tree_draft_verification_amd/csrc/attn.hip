@@ -40,6 +40,8 @@
 //   * Workgroup ids are remapped so that the blocks reading the same K/V rows
 //     run on the same die (shared L2).
 // fp32 kernel: a plain VALU kernel for small fp32 problems.
+#include <type_traits>
+
 #include "tv_internal.h"
 
 namespace tv {
@@ -54,6 +56,9 @@ constexpr int kKPad = 8;    // bf16 padding of a K row in LDS
 __device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) ^ d) & 15; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.f;  // rescale when a score exceeds the reference by 2^8
+// s_waitcnt operand: every counter at zero (all loads and LDS operations
+// of the wavefront complete)
+constexpr int kWaitAll0 = 0x0000;
 
 struct AttnArgs {
   const bf16_t* q;
@@ -117,10 +122,21 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int VI_TOTAL = (kKT / 4) * (D / 8);   // 4-key x 8-dim items of a V tile
   constexpr int VI = (VI_TOTAL + kThreads - 1) / kThreads;
   constexpr int kMaxAncNodes = kRows + 2;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[kKT * KROW];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[D * VROW];
+  // 128 rows with D = 128: K and V tiles go straight from memory into two
+  // LDS buffers each (unpadded, swizzled), and the ancestor words live in
+  // dynamic LDS sized to the tree; otherwise one padded K buffer and V^T,
+  // staged through registers.
+  constexpr bool kDma = (QBW == 2 && D == 128);
+  __shared__ __attribute__((aligned(1024))) bf16_t sK0[kKT * (kDma ? D : KROW)];
+  __shared__ __attribute__((aligned(1024))) bf16_t sK1[kDma ? kKT * D : 8];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV0[kDma ? kKT * D : D * VROW];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV1[kDma ? kKT * D : 8];
+  bf16_t* const sK = sK0;
+  bf16_t* const sVt = sV0;
   __shared__ int16_t sPar[TV_MAX_NODES];
-  __shared__ unsigned long long sAnc[kMaxAncNodes * (TV_MAX_NODES / 64)];
+  __shared__ unsigned long long sAncStatic[kDma ? 1 : kMaxAncNodes * (TV_MAX_NODES / 64)];
+  extern __shared__ unsigned long long sAncDyn[];
+  unsigned long long* const sAnc = kDma ? sAncDyn : sAncStatic;
   __shared__ unsigned sTreeMask;
   __shared__ int8_t sTreeList[TV_MAX_NODES / 64];
   __shared__ int sBT[PAGED ? kMaxPagedBlocks : 1];  // this workgroup's pages
@@ -323,38 +339,11 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // Tile loads.  The 128-row variant issues a tile's loads back to back and
-  // does not hold them across the products (its registers are full; with two
-  // workgroups per CU, one workgroup's loads overlap another's products).
-  // The 64-row variant has registers to spare and runs at small sizes with
-  // few workgroups per CU, so it issues the next tile's loads right after
-  // staging the current one and hides their latency behind the products.
-  constexpr bool kPrefetch = (QBW == 1);
-  if constexpr (kPrefetch) {
-    __syncthreads();  // tree tile list (and page entries) visible
-    if (n_tiles > 0) {
-      int k0r, n0, t0;
-      tile_rows(0, k0r, n0, t0);
-      load_tile(k0r, n0, t0 >= 0);
-    }
-  }
-  for (int it = 0; it < n_tiles; ++it) {
-    int krow0, nvalid, tt;
-    __syncthreads();  // previous tile consumed (first trip: tree tile list visible)
-    tile_rows(it, krow0, nvalid, tt);
+  // One tile's products once its K rows and V are in LDS (read through
+  // kfrag and vfrag): S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+  auto compute_tile = [&](int nvalid, int tt, auto kfrag, auto vfrag) {
     const bool tree = tt >= 0;
     const bool need_mask = tree || nvalid < kKT;
-    if constexpr (!kPrefetch) load_tile(krow0, nvalid, tree);
-    store_tile();
-    __syncthreads();  // this tile is in LDS
-    if constexpr (kPrefetch) {
-      if (it + 1 < n_tiles) {
-        int k1r, n1, t1;
-        tile_rows(it + 1, k1r, n1, t1);
-        load_tile(k1r, n1, t1 >= 0);
-      }
-    }
-
     // S^T = K Q^T: lane holds query column l16, keys kb*16 + 4*kg + r.
     f32x4_t s[QBW][4];
 #pragma unroll
@@ -364,7 +353,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) {
         Frag8 kf;
-        kf.u = *reinterpret_cast<const uint4*>(&sK[(kb * 16 + l16) * KROW + 32 * ks + 8 * kg]);
+        kf.u = kfrag(kb, ks);
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = mfma16x16x32(kf.v, qf[qb][ks], s[qb][kb]);
       }
@@ -426,15 +415,138 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int d = db * 16 + l16;
-        const bf16_t* vrow = &sVt[d * VROW];
         Frag8 vf;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((8 * u + kg) ^ vt_swz(d)) << 2));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((8 * u + kg + 4) ^ vt_swz(d)) << 2));
-        vf.u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        vf.u = vfrag(db, u);
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) o[qb][db] = mfma16x16x32(vf.v, pf[qb][u].v, o[qb][db]);
       }
+    }
+  };
+
+  if constexpr (kDma) {
+    // Tiles go straight from memory into LDS, the next tile's into the
+    // other buffer pair while this tile's products run; each tile ends
+    // waiting for the next one's loads (issued a tile of products earlier)
+    // and meeting at one barrier.  The buffers are separate LDS objects used
+    // with compile-time indices, so no read of one waits for loads into the
+    // other.  Layouts (16-byte pieces of a 256-byte row r):
+    //   K: piece x at position x ^ (r & 15): the fragment reads (16 rows,
+    //      one piece each) touch every bank once;
+    //   V: piece x at position x ^ 2 (r & 3): the transposing reads (4 rows
+    //      x 4 eight-byte units per 16 lanes) touch 32 distinct banks.
+    auto tdma = [&](bf16_t* kbuf, bf16_t* vbuf, int krow0, int nvalid, bool tree) {
+      const int last = krow0 + nvalid - 1;
+#pragma unroll
+      for (int i = 0; i < kKT / (4 * NW); ++i) {
+        const int r = (kKT / NW) * wave + 4 * i + (lane >> 4);
+        const size_t ro = row_off(min(krow0 + r, last), tree);
+        const int xk = (lane & 15) ^ (r & 15);
+        const int xv = (lane & 15) ^ (2 * (r & 3));
+        const int dst = ((kKT / NW) * wave + 4 * i) * D;
+        __builtin_amdgcn_global_load_lds((const void*)(a.k + ro + xk * 8),
+                                         (__attribute__((address_space(3))) void*)(kbuf + dst), 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(a.v + ro + xv * 8),
+                                         (__attribute__((address_space(3))) void*)(vbuf + dst), 16,
+                                         0, 0);
+      }
+    };
+    auto step = [&](int it, auto buf_tag) {
+      constexpr int U = decltype(buf_tag)::value;
+      const bf16_t* kb_lds = U ? sK1 : sK0;
+      const bf16_t* vb_lds = U ? sV1 : sV0;
+      int krow0, nvalid, tt;
+      tile_rows(it, krow0, nvalid, tt);
+      if (it + 1 < n_tiles) {
+        int k1r, n1, t1;
+        tile_rows(it + 1, k1r, n1, t1);
+        tdma(U ? sK0 : sK1, U ? sV0 : sV1, k1r, n1, t1 >= 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the next tile's loads go out first
+      // V^T operand rows d = db*16 + l16 for keys key0 .. key0+3: lane j of
+      // a 16-lane group points at key key0 + j/4, dims db*16 + 4 (j % 4) ..
+      // + 3, and the transposing read hands lane j dim db*16 + j of the four
+      // keys.
+      auto vtr = [&](int db, int key0) -> u32x2_t {
+        const int r = key0 + (l16 >> 2);
+        const int x = 2 * db + ((l16 & 3) >> 1);
+        const bf16_t* ptr = vb_lds + r * D + ((x ^ (2 * (r & 3))) * 8) + (l16 & 1) * 4;
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        const v4i16 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)ptr);
+        return __builtin_bit_cast(u32x2_t, t4);
+      };
+      compute_tile(
+          nvalid, tt,
+          [&](int kb, int ks) -> uint4 {
+            const int pos = (4 * ks + kg) ^ l16;  // row kb*16 + l16: (row & 15) == l16
+            return *reinterpret_cast<const uint4*>(kb_lds + (kb * 16 + l16) * D + pos * 8);
+          },
+          [&](int db, int u) -> uint4 {
+            const u32x2_t lo = vtr(db, 32 * u + 4 * kg);
+            const u32x2_t hi = vtr(db, 32 * u + 16 + 4 * kg);
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
+          });
+      // the next tile is in this wavefront's part of the buffers and its LDS
+      // reads of this tile are done; after the barrier, everyone's
+      __builtin_amdgcn_s_waitcnt(kWaitAll0);
+      __builtin_amdgcn_s_barrier();
+    };
+    __syncthreads();  // tree tile list (and page entries) visible
+    if (n_tiles > 0) {
+      int kr, nv, tq;
+      tile_rows(0, kr, nv, tq);
+      tdma(sK0, sV0, kr, nv, tq >= 0);
+      __builtin_amdgcn_s_waitcnt(kWaitAll0);
+      __builtin_amdgcn_s_barrier();
+    }
+    for (int it = 0; it < n_tiles; it += 2) {
+      step(it, std::integral_constant<int, 0>{});
+      if (it + 1 < n_tiles) step(it + 1, std::integral_constant<int, 1>{});
+    }
+  } else {
+    // Tile loads.  The 128-row variant issues a tile's loads back to back
+    // and does not hold them across the products (its registers are full;
+    // with two workgroups per CU, one workgroup's loads overlap another's
+    // products).  The 64-row variant has registers to spare and runs at
+    // small sizes with few workgroups per CU, so it issues the next tile's
+    // loads right after staging the current one and hides their latency
+    // behind the products.
+    constexpr bool kPrefetch = (QBW == 1);
+    if constexpr (kPrefetch) {
+      __syncthreads();  // tree tile list (and page entries) visible
+      if (n_tiles > 0) {
+        int k0r, n0, t0;
+        tile_rows(0, k0r, n0, t0);
+        load_tile(k0r, n0, t0 >= 0);
+      }
+    }
+    for (int it = 0; it < n_tiles; ++it) {
+      int krow0, nvalid, tt;
+      __syncthreads();  // previous tile consumed (first trip: tree tile list visible)
+      tile_rows(it, krow0, nvalid, tt);
+      if constexpr (!kPrefetch) load_tile(krow0, nvalid, tt >= 0);
+      store_tile();
+      __syncthreads();  // this tile is in LDS
+      if constexpr (kPrefetch) {
+        if (it + 1 < n_tiles) {
+          int k1r, n1, t1;
+          tile_rows(it + 1, k1r, n1, t1);
+          load_tile(k1r, n1, t1 >= 0);
+        }
+      }
+      compute_tile(
+          nvalid, tt,
+          [&](int kb, int ks) -> uint4 {
+            return *reinterpret_cast<const uint4*>(&sK[(kb * 16 + l16) * KROW + 32 * ks + 8 * kg]);
+          },
+          [&](int db, int u) -> uint4 {
+            const int d = db * 16 + l16;
+            const bf16_t* vrow = &sVt[d * VROW];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((8 * u + kg) ^ vt_swz(d)) << 2));
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((8 * u + kg + 4) ^ vt_swz(d)) << 2));
+            return make_uint4(lo.x, lo.y, hi.x, hi.y);
+          });
     }
   }
 
@@ -598,8 +710,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
 template <int D, bool PAGED>
 hipError_t launch_bf16(const AttnArgs& a, int qbw, hipStream_t stream) {
   const dim3 grid(a.total_blocks);
+  // the 128-row D = 128 variant keeps the ancestor words of its nodes (at
+  // most (rows - 1) / G + 2 of them) in dynamic LDS
+  const size_t anc_bytes =
+      (qbw == 2 && D == 128) ? (size_t)((a.rows - 1) / a.G + 2) * a.anc_words * 8 : 0;
   if (qbw == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4, PAGED>), grid, dim3(256), anc_bytes, stream, a);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4, PAGED>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
