@@ -37,6 +37,9 @@ ATTN_CASES = {
     "q8_ragged2_L2000_3100_N64": WORKLOADS["qwen3_8b_ragged8_N64"].replace(
         B=2, L_lo=2000, L_hi=3100, seed=22),
     "q8_bfs_L2049_N256": WORKLOADS["qwen3_8b_L16384_N256"].replace(L_lo=2049, L_hi=2049, seed=23),
+    # one query head per KV head: a 128-row block spans 128 nodes, whose
+    # ancestor words (3 per node) fill the most dynamic LDS
+    "g1_L2100_N130": Q8.replace(Hq=4, Hkv=4, L_lo=2100, L_hi=2100, N=130, seed=24),
 }
 
 
@@ -398,6 +401,7 @@ PAGED_CASES = {
     "empty_prefix_N20_ps16": ("empty_prefix_N20", 16),
     "g1_L64_N130_ps128": ("g1_L64_N130", 128),
     "q8_ragged2_L2000_3100_N64_ps16": ("q8_ragged2_L2000_3100_N64", 16),
+    "g1_L2100_N130_ps64": ("g1_L2100_N130", 64),
 }
 
 
