@@ -16,14 +16,15 @@
 //     products each lane owns one query column in both results, so the
 //     softmax state never moves between lanes and the probabilities feed the
 //     second product straight from registers (the key order inside a 32-wide
-//     k-step is permuted identically in V^T and P^T).  V is transposed on its
-//     way into LDS.
-//   * A tile's loads are issued back to back and are unconditional (rows
-//     past the valid range are clamped to a valid row and masked out of the
-//     scores), so they are all in flight at once; they are not held in
-//     registers across the products, which keeps the kernel at two or more
-//     workgroups per CU so that one workgroup's loads overlap another's
-//     products.
+//     k-step is permuted identically in V^T and P^T).
+//   * D = 128: a tile's K and V rows go straight from memory into LDS
+//     (global_load_lds), the next tile's into a second buffer pair while
+//     this tile's products run; V stays row-major and the V^T operand comes
+//     from the transposing LDS read of gfx950 (ds_read_b64_tr_b16).  D = 64:
+//     tiles are staged through registers and V is transposed on its way
+//     into LDS.  Loads are unconditional (rows past the valid range are
+//     clamped to a valid row and masked out of the scores), so a tile's
+//     loads are all in flight at once.
 //   * Softmax in the exp2 domain: one FMA folds the scale and the running
 //     max, then v_exp_f32; probabilities go to bf16 with v_cvt_pk_bf16_f32.
 //     The running reference max moves only when a wavefront sees a score more
@@ -122,11 +123,11 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int VI_TOTAL = (kKT / 4) * (D / 8);   // 4-key x 8-dim items of a V tile
   constexpr int VI = (VI_TOTAL + kThreads - 1) / kThreads;
   constexpr int kMaxAncNodes = kRows + 2;
-  // 128 rows with D = 128: K and V tiles go straight from memory into two
-  // LDS buffers each (unpadded, swizzled), and the ancestor words live in
-  // dynamic LDS sized to the tree; otherwise one padded K buffer and V^T,
-  // staged through registers.
-  constexpr bool kDma = (QBW == 2 && D == 128);
+  // D = 128: K and V tiles go straight from memory into two LDS buffers
+  // each (unpadded, swizzled), and the ancestor words live in dynamic LDS
+  // sized to the tree; D = 64: one padded K buffer and V^T, staged through
+  // registers.
+  constexpr bool kDma = (D == 128);
   __shared__ __attribute__((aligned(1024))) bf16_t sK0[kKT * (kDma ? D : KROW)];
   __shared__ __attribute__((aligned(1024))) bf16_t sK1[kDma ? kKT * D : 8];
   __shared__ __attribute__((aligned(1024))) bf16_t sV0[kDma ? kKT * D : D * VROW];
@@ -505,13 +506,12 @@ void attn_bf16_kernel(AttnArgs a) {
       if (it + 1 < n_tiles) step(it + 1, std::integral_constant<int, 1>{});
     }
   } else {
-    // Tile loads.  The 128-row variant issues a tile's loads back to back
-    // and does not hold them across the products (its registers are full;
-    // with two workgroups per CU, one workgroup's loads overlap another's
-    // products).  The 64-row variant has registers to spare and runs at
-    // small sizes with few workgroups per CU, so it issues the next tile's
-    // loads right after staging the current one and hides their latency
-    // behind the products.
+    // D = 64, tiles staged through registers.  The 128-row variant issues a
+    // tile's loads back to back and does not hold them across the products
+    // (with two workgroups per CU, one workgroup's loads overlap another's
+    // products).  The 64-row variant runs at small sizes with few
+    // workgroups per CU, so it issues the next tile's loads right after
+    // staging the current one and hides their latency behind the products.
     constexpr bool kPrefetch = (QBW == 1);
     if constexpr (kPrefetch) {
       __syncthreads();  // tree tile list (and page entries) visible
@@ -710,14 +710,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(
 template <int D, bool PAGED>
 hipError_t launch_bf16(const AttnArgs& a, int qbw, hipStream_t stream) {
   const dim3 grid(a.total_blocks);
-  // the 128-row D = 128 variant keeps the ancestor words of its nodes (at
-  // most (rows - 1) / G + 2 of them) in dynamic LDS
-  const size_t anc_bytes =
-      (qbw == 2 && D == 128) ? (size_t)((a.rows - 1) / a.G + 2) * a.anc_words * 8 : 0;
+  // the D = 128 variants keep the ancestor words of their nodes (at most
+  // (rows - 1) / G + 2 of them) in dynamic LDS
+  const size_t anc_bytes = D == 128 ? (size_t)((a.rows - 1) / a.G + 2) * a.anc_words * 8 : 0;
   if (qbw == 2)
     hipLaunchKernelGGL((attn_bf16_kernel<D, 2, 4, PAGED>), grid, dim3(256), anc_bytes, stream, a);
   else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4, PAGED>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, 1, 4, PAGED>), grid, dim3(256), anc_bytes, stream, a);
   return hipGetLastError();
 }
 
