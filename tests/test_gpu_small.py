@@ -87,8 +87,13 @@ def test_attention_chain_and_star_trees(shape):
     assert_attn_close(to_host_f64(out), ref, shape)
 
 
-def test_attention_deep_chain_1024_nodes():
-    wl = A3B.replace(B=1, Hq=8, Hkv=1, L_lo=40, L_hi=40, N=1024, seed=22)
+@pytest.mark.parametrize("hq,hkv,L", [(8, 1, 40), (2, 2, 2100)],
+                         ids=["g8_L40", "g1_L2100"])
+def test_attention_deep_chain_1024_nodes(hq, hkv, L):
+    """A 1024-node chain: every tree tile visible to the deepest nodes; with
+    one query head per KV head and a long prefix, each 128-row block spans
+    128 nodes with 16 ancestor words each (the largest ancestor table)."""
+    wl = A3B.replace(B=1, Hq=hq, Hkv=hkv, L_lo=L, L_hi=L, N=1024, seed=22)
     a = attn_inputs(wl)
     parent = np.arange(-1, 1023, dtype=np.int32)[None]
     out = _run_attn(a, wl, parent=parent)
