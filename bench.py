@@ -339,7 +339,7 @@ def main():
     traffic = None
     if os.path.exists(COUNTERS):
         with open(COUNTERS) as f:
-            cnt = json.load(f).get("lmhead_bf16_kernel", {})
+            cnt = json.load(f).get("lmhead_argmax", {})
         if (cnt.get("workload") == wl.name
                 and cnt.get("source_digest") == kernel_source_digest(LMHEAD_SOURCES)):
             traffic = cnt.get("traffic_bytes")
@@ -353,7 +353,13 @@ def main():
         achieved = lm_b / (lm_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
-    roof.update(kernel="lmhead_bf16_kernel<packed>" if wl.dtype == "bf16" else "lmhead_f32_kernel",
+    if wl.dtype != "bf16":
+        lm_kernel = "lmhead_f32_kernel"
+    elif wl.M <= 64:
+        lm_kernel = "lmhead_stream_kernel (packed W)"
+    else:
+        lm_kernel = ("gemm32w_kernel" if wl.M >= 512 else "gemm32_kernel") + " + argmax_reduce_kernel"
+    roof.update(kernel=lm_kernel,
                 algorithmic_bytes=lm_b, launch_us=round(lm_us, 2))
 
     res = {

@@ -31,6 +31,11 @@
 //   * Workgroups that share a vocabulary tile (different 64-row slices of
 //     hidden states) get adjacent logical ids, which the remap places on one
 //     die so that the tile comes from HBM once and from that die's L2 after.
+//   * With the packed layout and M <= 64 (the LM head of a verification
+//     step) the same products run as a persistent stream,
+//     lmhead_stream_kernel: as many workgroups as stay resident, each
+//     walking its share of the tiles as one stream of k chunks, so no
+//     workgroup ramps up, drains or finishes per tile.
 #include "tv_internal.h"
 
 namespace tv {
@@ -40,6 +45,9 @@ constexpr int kThreads = 256;
 constexpr int kVT = 128;        // vocabulary rows per workgroup (32 per wavefront)
 constexpr int kKC = 128;        // k per pipeline stage
 constexpr int kHRow = kKC + 8;  // LDS row of the hidden-state slice (bf16)
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt left at their maxima
+// (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x, int off) {
   const uint32_t lo = __shfl_xor((uint32_t)x, off, 64);
@@ -47,23 +55,29 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x,
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Fold this workgroup's per-row keys into the global keys; the last
-// workgroup converts them to indices and leaves the workspace zeroed.  The
-// atomics return their old value and that value is consumed before the
-// barrier, so every key update of a workgroup has completed before its
-// counter increment is issued; no device-wide fence (and no L2 write-back)
-// is needed.
-__device__ __forceinline__ void argmax_commit(unsigned long long* keys, unsigned* counter,
-                                              int32_t* argmax, int M, int total_blocks, int m0,
-                                              int mt, const unsigned long long* s_rowkey) {
-  __shared__ int s_last;
+// Fold a tile's per-row keys into the global keys.  The atomics return
+// their old value and that value is consumed, so each one has completed
+// before the thread passes the next barrier.
+__device__ __forceinline__ void fold_row_keys(unsigned long long* keys, int M, int m0, int mt,
+                                              const unsigned long long* s_rowkey) {
+  __shared__ volatile int s_sink;  // volatile: the store below (and so the wait) stays
   const int tid = threadIdx.x;
   if (tid < mt && m0 + tid < M) {
     const unsigned long long old = __hip_atomic_fetch_max(
         &keys[m0 + tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == 1ull) s_last = 0;  // never true (keys exceed 2^32); forces the wait
+    if (old == 1ull) s_sink = 0;  // never true (keys exceed 2^32); forces the wait
   }
-  __syncthreads();
+}
+
+// After every key update of the workgroup (a barrier past fold_row_keys):
+// count the workgroup as done; the last of `total_blocks` converts the keys
+// to indices and leaves the workspace zeroed.  Every key update of a
+// workgroup has completed before its counter increment is issued, so no
+// device-wide fence (and no L2 write-back) is needed.
+__device__ __forceinline__ void finish_argmax(unsigned long long* keys, unsigned* counter,
+                                              int32_t* argmax, int M, int total_blocks) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
   if (tid == 0) {
     const unsigned prev =
         __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -77,6 +91,15 @@ __device__ __forceinline__ void argmax_commit(unsigned long long* keys, unsigned
     argmax[m] = (int32_t)(~(uint32_t)(k & 0xffffffffull));
   }
   if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup's keys folded, then the finish.
+__device__ __forceinline__ void argmax_commit(unsigned long long* keys, unsigned* counter,
+                                              int32_t* argmax, int M, int total_blocks, int m0,
+                                              int mt, const unsigned long long* s_rowkey) {
+  fold_row_keys(keys, M, m0, mt, s_rowkey);
+  __syncthreads();
+  finish_argmax(keys, counter, argmax, M, total_blocks);
 }
 
 // Address of piece s (16 bytes) of lane `lane` of 16-row block j of tile vt,
@@ -366,6 +389,167 @@ void lmhead_bf16_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
   }
 }
 
+// Persistent form of the packed M <= 64 argmax (the LM head of a
+// verification step).  Each workgroup walks the vocabulary tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ... as one stream of k chunks: the
+// W ring runs across tile boundaries, so the next tile's first chunks are
+// in flight while a tile's epilogue folds its keys, and no workgroup ramps
+// up or drains per tile.  The grid is what stays resident at once (about
+// 3 workgroups per CU), measured 5 % faster than one workgroup per tile.
+// Products, operand layouts, the key fold and the last-workgroup finish
+// are those of lmhead_bf16_kernel.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void lmhead_stream_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
+                          int32_t* __restrict__ argmax, float* __restrict__ logits,
+                          unsigned long long* __restrict__ keys, unsigned* __restrict__ counter,
+                          int M, int K, int V, int ntiles) {
+  constexpr int MB = 4;
+  constexpr int kRowsM = 16 * MB;
+  constexpr int HP = kRowsM * (kKC / 8) / kThreads;
+  __shared__ __attribute__((aligned(16))) bf16_t sH[2][kRowsM * kHRow];
+  __shared__ unsigned long long s_wkey[4][kRowsM];
+  __shared__ unsigned long long s_rowkey[kRowsM];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int kg = lane >> 4;
+  const int nk = K / kKC;  // even: K is a multiple of 256
+  const int ntl = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int G = ntl * nk;  // chunks of this workgroup's stream
+  // chunk g of the stream: chunk g % nk of tile blockIdx.x + (g / nk) gridDim.x
+  auto wload = [&](int g, int vb, int s) -> u32x4_t {
+    const int j = g / nk;
+    const int c = g - j * nk;
+    const int vt = blockIdx.x + j * gridDim.x;
+    return __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_t*>(W + packed_offset(vt, c, nk, wave * 2 + vb, s, lane)));
+  };
+  const bf16_t* hsrc[HP];
+  int hdst[HP];
+#pragma unroll
+  for (int i = 0; i < HP; ++i) {
+    const int c = tid + i * kThreads;
+    const int r = c >> 4;
+    const int x = c & 15;
+    hsrc[i] = H + (size_t)(r < M ? r : M - 1) * K + x * 8;
+    hdst[i] = r * kHRow + x * 8;
+  }
+
+  u32x4_t wb[2][2][4];  // [ring slot][16-row block][piece]
+  u32x4_t hreg[HP];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) wb[d][vb][s] = wload(min(d, G - 1), vb, s);
+#pragma unroll
+  for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const u32x4_t*>(hsrc[i]);
+#pragma unroll
+  for (int i = 0; i < HP; ++i) *reinterpret_cast<u32x4_t*>(&sH[0][hdst[i]]) = hreg[i];
+  __syncthreads();
+
+  f32x4_t acc[2][MB];
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[vb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int g0 = 0; g0 < G; g0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int g = g0 + u;
+      const int c = g % nk;
+      // every tile uses the same H rows: the next chunk's slice is chunk
+      // c + 1, or chunk 0 of the next tile
+      const int ch = c + 1 == nk ? 0 : c + 1;
+#pragma unroll
+      for (int i = 0; i < HP; ++i) hreg[i] = *reinterpret_cast<const u32x4_t*>(hsrc[i] + ch * kKC);
+      const bf16_t* sh = sH[u];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          Frag8 hf;
+          hf.u = *reinterpret_cast<const uint4*>(&sh[(mb * 16 + l16) * kHRow + 32 * kg + 8 * s]);
+#pragma unroll
+          for (int vb = 0; vb < 2; ++vb) {
+            Frag8 wf;
+            wf.q = wb[u][vb][s];
+            acc[vb][mb] = mfma16x16x32(wf.v, hf.v, acc[vb][mb]);
+          }
+        }
+      }
+      const int gw = min(g + 2, G - 1);  // past the end: reload the last chunk
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) wb[u][vb][s] = wload(gw, vb, s);
+#pragma unroll
+      for (int i = 0; i < HP; ++i) *reinterpret_cast<u32x4_t*>(&sH[u ^ 1][hdst[i]]) = hreg[i];
+      __syncthreads();
+      if (u == 1 && c == nk - 1) {
+        // a tile is complete (its last chunk is odd): fold its per-row keys
+        // (and write its logits, when asked), then start the next from zero
+        const int v0 = (blockIdx.x + (g / nk) * gridDim.x) * kVT;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int m = mb * 16 + l16;
+          unsigned long long best = 0ull;
+#pragma unroll
+          for (int vb = 0; vb < 2; ++vb) {
+            const int vbase = v0 + wave * 32 + vb * 16 + 4 * kg;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int v = vbase + r;
+              if (v < V) {
+                const unsigned long long key = argmax_key(acc[vb][mb][r], (uint32_t)v);
+                best = key > best ? key : best;
+              }
+            }
+            if (logits != nullptr && m < M) {
+              float* dst = logits + (size_t)m * V + vbase;
+              if ((V & 3) == 0 && vbase + 3 < V) {
+                *reinterpret_cast<f32x4_t*>(dst) = acc[vb][mb];
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (vbase + r < V) dst[r] = acc[vb][mb][r];
+              }
+            }
+            acc[vb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+          unsigned long long o = shfl_xor_u64(best, 16);
+          best = o > best ? o : best;
+          o = shfl_xor_u64(best, 32);
+          best = o > best ? o : best;
+          if (kg == 0) s_wkey[wave][m] = best;
+        }
+        __syncthreads();
+        if (tid < kRowsM) {
+          unsigned long long k = s_wkey[0][tid];
+#pragma unroll
+          for (int w = 1; w < 4; ++w) k = s_wkey[w][tid] > k ? s_wkey[w][tid] : k;
+          s_rowkey[tid] = k;
+        }
+        // (s_wkey and s_rowkey are rewritten only a whole tile of barriers
+        // later).  The fold does not wait for its atomics, so the next
+        // tile's W loads already in flight are not drained here.
+        if (tid < kRowsM && tid < M)
+          __hip_atomic_fetch_max(&keys[tid], s_rowkey[tid], __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // every key atomic of this wavefront has completed (its acknowledgement
+  // counts in vmcnt), then every wavefront's: only then the finish
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  finish_argmax(keys, counter, argmax, M, gridDim.x);
+}
+
 // Finish of the partial-key form: one wavefront per row takes the maximum
 // over the row's per-tile keys.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const unsigned long long* __restrict__ part,
@@ -519,6 +703,26 @@ hipError_t launch_pack_gate_up(const void* w, void* packed, int inter, int K,
   return hipGetLastError();
 }
 
+
+// Workgroups of lmhead_stream_kernel resident at once on the current device
+// (its grid), queried once per device.
+static int stream_grid() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lmhead_stream_kernel, kThreads, 0) !=
+            hipSuccess || per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    cached[dev] = per_cu * cus;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
                                 float* logits, int M, int K, int V, int dtype, int w_layout,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -558,6 +762,12 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
 #define TV_LM_LAUNCH(P, MBV, MODEV)                                                         \
   hipLaunchKernelGGL((lmhead_bf16_kernel<P, MBV, MODEV>), grid, block, 0, stream, h, wv, argmax, \
                      logits, keys, counter, M, K, V, nmt, total, nullptr, 1, nullptr, 0)
+  if (mb == 4 && pk) {
+    const int g = stream_grid();
+    hipLaunchKernelGGL(lmhead_stream_kernel, dim3(nvt < g ? nvt : g), block, 0, stream, h, wv,
+                       argmax, logits, keys, counter, M, K, V, nvt);
+    return hipGetLastError();
+  }
   if (mb == 4) {
     if (pk) TV_LM_LAUNCH(true, 4, kArgmaxCommit); else TV_LM_LAUNCH(false, 4, kArgmaxCommit);
   } else {
