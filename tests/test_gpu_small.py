@@ -141,6 +141,11 @@ LM_CASES = {
     "M256_K512_V4163": Q8.replace(N=256, hidden=512, V=4163, seed=34),
     "M513_K256_V2000": Q8.replace(B=1, N=513, hidden=256, V=2000, seed=35),
     "f32_M40_K100_V777": Q8.replace(dtype="f32", N=40, hidden=100, V=777, seed=36),
+    # more 128-row tiles than resident workgroups, so each workgroup of the
+    # persistent M <= 64 kernel walks several tiles; the shortest k stream
+    "M64_K256_V151936": Q8.replace(N=64, hidden=256, V=151936, seed=37),
+    # ragged last tile (33 rows) after 781 whole ones
+    "M17_K512_V100001": Q8.replace(B=1, N=17, hidden=512, V=100001, seed=38),
 }
 
 

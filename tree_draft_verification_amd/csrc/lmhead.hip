@@ -56,16 +56,15 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long x,
 }
 
 // Fold a tile's per-row keys into the global keys.  The atomics return
-// their old value and that value is consumed, so each one has completed
-// before the thread passes the next barrier.
+// their old value and an empty asm statement takes it as an input, so the
+// compiler waits for each one to complete before the thread goes on.
 __device__ __forceinline__ void fold_row_keys(unsigned long long* keys, int M, int m0, int mt,
                                               const unsigned long long* s_rowkey) {
-  __shared__ volatile int s_sink;  // volatile: the store below (and so the wait) stays
   const int tid = threadIdx.x;
   if (tid < mt && m0 + tid < M) {
     const unsigned long long old = __hip_atomic_fetch_max(
         &keys[m0 + tid], s_rowkey[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == 1ull) s_sink = 0;  // never true (keys exceed 2^32); forces the wait
+    asm volatile("" ::"v"(old));
   }
 }
 

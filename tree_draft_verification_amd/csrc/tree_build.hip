@@ -165,6 +165,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_build_kernel(
   __shared__ float s_clp[kMaxDepth][kMaxW];
   __shared__ int s_fidx[kMaxW];
   __shared__ double s_fscore[kMaxW];
+  __shared__ double s_escore[64];            // eligible children of a level (see B)
+  __shared__ int s_eidx[64];
   __shared__ int s_wsum[kTreeThreads / 64];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -196,7 +198,17 @@ __global__ __launch_bounds__(kTreeThreads) void tree_build_kernel(
   // B. breadth-first levels, all in wavefront 0 (LDS accesses of one
   // wavefront are ordered, so no barrier is needed between levels): the
   // children of the frontier in generation order, then the next frontier
-  // by rank counting (score descending, then generation)
+  // by rank counting (score descending, then generation).
+  // Only children (r, j) with (r + 1)(j + 1) <= W can reach the frontier:
+  // the frontier (by rank) and the candidate log-probabilities are both in
+  // descending order and fp64 addition is monotone, so the other children
+  // (r', j') with r' <= r and j' <= j score at least as high and come
+  // earlier in generation order, which puts (r, j) at rank >= (r+1)(j+1)-1.
+  // The W best children are therefore all eligible, and every child that
+  // beats an eligible child ranked below W is eligible too: ranks counted
+  // among the eligible children (kept in generation order) are the true
+  // ranks wherever they are below W, and at least W elsewhere.  At most
+  // sum_r floor(W / (r + 1)) <= 50 children are eligible (W <= 16).
   if (wave == 0) {
     if (lane == 0) {
       s_fidx[0] = -1;
@@ -212,27 +224,31 @@ __global__ __launch_bounds__(kTreeThreads) void tree_build_kernel(
         s_tok[base + t] = s_ctok[d - 1][j];
         s_dep[base + t] = (int8_t)d;
       }
-      int nidx[4];
-      double nsc[4];
-      int nrank[4];
+      int ne = 0;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {  // lsz <= 256: up to four children per lane
         const int t = lane + 64 * q;
-        nrank[q] = kMaxW;
-        if (t < lsz) {
-          const double sc = s_score[base + t];
-          nrank[q] = rank_among(s_score + base, lsz, sc, t);
-          nidx[q] = base + t;
-          nsc[q] = sc;
+        const int r = t / W, j = t - (t / W) * W;
+        const bool el = t < lsz && (r + 1) * (j + 1) <= W;
+        const u64 m = __ballot(el);
+        if (el) {
+          const int k = ne + __popcll(m & ((1ull << lane) - 1ull));
+          s_escore[k] = s_score[base + t];
+          s_eidx[k] = base + t;
         }
+        ne += __popcll(m);
+      }
+      int nrank = kMaxW, nidx = 0;
+      double nsc = 0.0;
+      if (lane < ne) {
+        nsc = s_escore[lane];
+        nidx = s_eidx[lane];
+        nrank = rank_among(s_escore, ne, nsc, lane);
       }
       // every read of the old frontier is done before it is overwritten
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (nrank[q] < W) {
-          s_fidx[nrank[q]] = nidx[q];
-          s_fscore[nrank[q]] = nsc[q];
-        }
+      if (nrank < W) {
+        s_fidx[nrank] = nidx;
+        s_fscore[nrank] = nsc;
       }
       fsize = lsz < W ? lsz : W;
       base += lsz;
@@ -244,10 +260,63 @@ __global__ __launch_bounds__(kTreeThreads) void tree_build_kernel(
   __syncthreads();  // s_wsum is reused by the scan
 
   // C. keep the `budget` best candidates (score descending, then pool
-  // index, i.e. depth and generation): bitonic sort of the pool
-  {
-    int P2 = 1;
-    while (P2 < C) P2 <<= 1;
+  // index, i.e. depth and generation): bitonic sort of the pool.  Up to one
+  // entry per thread, each thread keeps its entry in registers: the steps
+  // between lanes of one wavefront (partner distance < 64) exchange by
+  // shuffles, and only the longer ones go through LDS between two barriers
+  // (10 of the 55 steps at 1024 entries).
+  int P2 = 1;
+  while (P2 < C) P2 <<= 1;
+  if (P2 <= kTreeThreads) {
+    double sc = tid < C ? s_score[tid] : -INFINITY;
+    int id = tid;
+    for (int k = 2; k <= P2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        double so;
+        int io;
+        if (j >= 64) {
+          __syncthreads();  // the previous step's reads are done
+          if (tid < P2) {
+            s_score[tid] = sc;
+            s_id[tid] = (int16_t)id;
+          }
+          __syncthreads();
+          so = s_score[(tid ^ j) & (P2 - 1)];
+          io = s_id[(tid ^ j) & (P2 - 1)];
+        } else {
+          const long long b = __double_as_longlong(sc);
+          const uint32_t lo = __shfl_xor((uint32_t)b, j, 64);
+          const uint32_t hi = __shfl_xor((uint32_t)((unsigned long long)b >> 32), j, 64);
+          so = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+          io = __shfl_xor(id, j, 64);
+        }
+        // the lower index of a pair ends with the better entry in a
+        // descending block ((index & k) == 0), with the worse in an
+        // ascending one; ids are distinct, so entries never compare equal
+        const bool o_better = so > sc || (so == sc && io < id);
+        const bool lower = (tid & j) == 0;
+        const bool desc = (tid & k) == 0;
+        if (lower == desc ? o_better : !o_better) {
+          sc = so;
+          id = io;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < P2) {
+      s_score[tid] = sc;
+      s_id[tid] = (int16_t)id;
+    }
+    __syncthreads();
+    for (int i = tid; i < C; i += kTreeThreads) s_node[i] = -1;
+    __syncthreads();
+    for (int r = tid; r < budget; r += kTreeThreads) {
+      const int id2 = s_id[r];
+      s_node[id2] = 1;
+      s_kscore[id2] = (float)s_score[r];
+    }
+    __syncthreads();
+  } else {
     for (int i = tid; i < P2; i += kTreeThreads) {
       s_id[i] = (int16_t)i;
       if (i >= C) s_score[i] = -INFINITY;
