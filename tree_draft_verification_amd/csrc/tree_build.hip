@@ -93,6 +93,27 @@ struct WaveList {
   }
 };
 
+// The wavefront's 64 keys in descending order across the lanes (bitonic
+// network over lane indices, exchanges by shuffles).
+__device__ __forceinline__ u64 wave_sort_desc(u64 k, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)k, j, 64);
+      const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), j, 64);
+      const u64 o = ((u64)hi << 32) | lo;
+      // the lower lane of a pair keeps the larger key in a descending
+      // block ((lane & size) == 0), the smaller in an ascending one
+      const bool lower = (lane & j) == 0;
+      const bool desc = (lane & size) == 0;
+      const u64 big = o > k ? o : k, small = o > k ? k : o;
+      k = (lower == desc) ? big : small;
+    }
+  }
+  return k;
+}
+
 // Rank of (v, i) among a[0..n) in LDS: entries greater than v, or equal to
 // it at a smaller index.  Eight independent reads per trip (the count is
 // bound by LDS latency otherwise; more would exceed the register budget of
@@ -123,9 +144,14 @@ __global__ __launch_bounds__(kTopThreads) void draft_topk_kernel(
   const int v1 = min(V, v0 + chunk_len);
   const float* x = logp + (size_t)row * V;
   WaveList wl;
-  // eight independent loads per trip (clamped addresses), then the offers;
-  // the trip count is uniform across the wavefront (offer() uses ballots)
-  constexpr int kBatch = 8;
+  // kBatch independent loads per trip (clamped addresses; one trip covers a
+  // 6144-element chunk), then the offers; the trip count is uniform across
+  // the wavefront (offer() uses ballots).  The list starts from the first
+  // 64 keys sorted across the lanes, which fills it and sets its threshold
+  // without one insertion per key; keys are unique, so the list ends the
+  // same whatever the order of the offers.
+  constexpr int kBatch = 24;
+  bool first = true;
   for (int b0 = v0 + wave * 64; b0 < v1; b0 += kBatch * kTopThreads) {
     float val[kBatch];
 #pragma unroll
@@ -135,17 +161,22 @@ __global__ __launch_bounds__(kTopThreads) void draft_topk_kernel(
       const int v = b0 + u * kTopThreads + lane;
       // + 0.0f turns -0.0 into +0.0, so equal values tie on the token id
       const u64 k = v < v1 ? argmax_key(val[u] + 0.0f, (uint32_t)v) : 0ull;
-      wl.offer(k, 0, W, lane);
+      if (u == 0 && first) {
+        const u64 sk = wave_sort_desc(k, lane);
+        wl.L = lane < W ? sk : 0ull;
+        wl.thr = readlane_u64(sk, W - 1);
+        first = false;
+      } else {
+        wl.offer(k, 0, W, lane);
+      }
     }
   }
   if (lane < W) s_wl[wave][lane] = wl.L;
   __syncthreads();
-  if (wave == 0) {  // merge the four lists (keys are unique)
+  if (wave == 0) {  // merge the four lists (4 W <= 64 unique keys): sort them
     const int n = (kTopThreads / 64) * W;
-    WaveList m;
-    const u64 k = lane < n ? s_wl[lane / W][lane % W] : 0ull;
-    m.offer(k, 0, W, lane);
-    if (lane < W) part[(size_t)blockIdx.x * kMaxW + lane] = m.L;
+    const u64 k = wave_sort_desc(lane < n ? s_wl[lane / W][lane % W] : 0ull, lane);
+    if (lane < W) part[(size_t)blockIdx.x * kMaxW + lane] = k;
   }
 }
 
@@ -185,8 +216,13 @@ __global__ __launch_bounds__(kTreeThreads) void tree_build_kernel(
   const int nl = nch * W;
   for (int d = wave; d < D; d += kWaves) {
     const u64* lists = s_lists + (size_t)d * nl;
+    // the first 64 keys sorted across the lanes start the list (as in
+    // kernel 1), the rest are offered
     WaveList m;
-    for (int i0 = 0; i0 < nl; i0 += 64)
+    const u64 sk = wave_sort_desc(lane < nl ? lists[lane] : 0ull, lane);
+    m.L = lane < W ? sk : 0ull;
+    m.thr = readlane_u64(sk, W - 1);
+    for (int i0 = 64; i0 < nl; i0 += 64)
       m.offer(i0 + lane < nl ? lists[i0 + lane] : 0ull, 0, W, lane);
     if (lane < W) {
       s_ctok[d][lane] = key_token(m.L);
