@@ -28,6 +28,13 @@ CASES.update({
     "b3_d10_w6_n200_ties": TreeBuildConfig("ties", B=3, depth=10, width=6, budget=200, V=64,
                                            scale=1.0, quantum=0.5, seed=15),
     "b1_d2_w3_n3_V3": TreeBuildConfig("tiny", B=1, depth=2, width=3, budget=3, V=3, seed=16),
+    # widest frontier with a pool under 1024 (register sort): 50 eligible
+    # children per level, the most the level step handles
+    "b2_d3_w16_n400_V4000": TreeBuildConfig("w16s", B=2, depth=3, width=16, budget=400, V=4000,
+                                            seed=17),
+    # tie-heavy log-probabilities at width 16 (equal scores across parents)
+    "b2_d4_w16_n500_ties": TreeBuildConfig("w16t", B=2, depth=4, width=16, budget=500, V=300,
+                                           scale=1.0, quantum=0.25, seed=18),
 })
 
 
