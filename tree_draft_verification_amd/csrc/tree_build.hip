@@ -296,60 +296,66 @@ __global__ __launch_bounds__(kTreeThreads) void tree_build_kernel(
   __syncthreads();  // s_wsum is reused by the scan
 
   // C. keep the `budget` best candidates (score descending, then pool
-  // index, i.e. depth and generation): bitonic sort of the pool.  Up to one
-  // entry per thread, each thread keeps its entry in registers: the steps
-  // between lanes of one wavefront (partner distance < 64) exchange by
-  // shuffles, and only the longer ones go through LDS between two barriers
-  // (10 of the 55 steps at 1024 entries).
+  // index, i.e. depth and generation).  Only the kept set matters (the
+  // nodes are numbered in pool order), so up to 1024 entries need no global
+  // sort: each wavefront sorts its 64 entries across its lanes (shuffle
+  // bitonic network), and an entry's rank is its place in its own list plus,
+  // for every other list, the number of entries there that beat it (a binary
+  // search; the lists are sorted by the same order).  Larger pools sort in
+  // LDS.
   int P2 = 1;
   while (P2 < C) P2 <<= 1;
-  if (P2 <= kTreeThreads) {
+  if (C <= kTreeThreads) {
     double sc = tid < C ? s_score[tid] : -INFINITY;
     int id = tid;
-    for (int k = 2; k <= P2; k <<= 1) {
+    // entry (so, io) beats (sc, id): higher score, or equal and earlier
+    for (int k = 2; k <= 64; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        double so;
-        int io;
-        if (j >= 64) {
-          __syncthreads();  // the previous step's reads are done
-          if (tid < P2) {
-            s_score[tid] = sc;
-            s_id[tid] = (int16_t)id;
-          }
-          __syncthreads();
-          so = s_score[(tid ^ j) & (P2 - 1)];
-          io = s_id[(tid ^ j) & (P2 - 1)];
-        } else {
-          const long long b = __double_as_longlong(sc);
-          const uint32_t lo = __shfl_xor((uint32_t)b, j, 64);
-          const uint32_t hi = __shfl_xor((uint32_t)((unsigned long long)b >> 32), j, 64);
-          so = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-          io = __shfl_xor(id, j, 64);
-        }
-        // the lower index of a pair ends with the better entry in a
-        // descending block ((index & k) == 0), with the worse in an
-        // ascending one; ids are distinct, so entries never compare equal
+        const long long bits = __double_as_longlong(sc);
+        const uint32_t lo = __shfl_xor((uint32_t)bits, j, 64);
+        const uint32_t hi = __shfl_xor((uint32_t)((unsigned long long)bits >> 32), j, 64);
+        const double so = __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+        const int io = __shfl_xor(id, j, 64);
+        // the lower lane of a pair ends with the better entry in a
+        // descending block ((lane & k) == 0), the worse in an ascending one
         const bool o_better = so > sc || (so == sc && io < id);
-        const bool lower = (tid & j) == 0;
-        const bool desc = (tid & k) == 0;
+        const bool lower = (lane & j) == 0;
+        const bool desc = (lane & k) == 0;
         if (lower == desc ? o_better : !o_better) {
           sc = so;
           id = io;
         }
       }
     }
+    // each wavefront read only its own 64 entries: its sorted list replaces them
+    s_score[tid] = sc;
+    s_id[tid] = (int16_t)id;
+    if (tid < C) s_node[tid] = -1;
     __syncthreads();
-    if (tid < P2) {
-      s_score[tid] = sc;
-      s_id[tid] = (int16_t)id;
-    }
-    __syncthreads();
-    for (int i = tid; i < C; i += kTreeThreads) s_node[i] = -1;
-    __syncthreads();
-    for (int r = tid; r < budget; r += kTreeThreads) {
-      const int id2 = s_id[r];
-      s_node[id2] = 1;
-      s_kscore[id2] = (float)s_score[r];
+    const int nl = (C + 63) / 64;
+    if (id < C) {
+      int rank = lane;
+      for (int w = 0; w < nl; ++w) {
+        if (w == wave) continue;
+        const double* ls = s_score + w * 64;
+        const int16_t* li = s_id + w * 64;
+        int lo = 0, hi = 64;  // entries [0, lo) beat (sc, id), [hi, 64) do not
+#pragma unroll
+        for (int step = 0; step < 7; ++step) {  // 65 possible counts
+          if (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            const double sm = ls[mid];
+            const bool beats = sm > sc || (sm == sc && li[mid] < id);
+            lo = beats ? mid + 1 : lo;
+            hi = beats ? hi : mid;
+          }
+        }
+        rank += lo;
+      }
+      if (rank < budget) {
+        s_node[id] = 1;
+        s_kscore[id] = (float)sc;
+      }
     }
     __syncthreads();
   } else {
