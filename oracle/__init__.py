@@ -29,7 +29,7 @@ from .verify import (  # noqa: F401
     tree_attention_paged,
     verify_step,
 )
-from .tree_build import accum_logp_tree, topk_tokens  # noqa: F401
+from .tree_build import accum_logp_tree, accum_logp_tree_paths, topk_tokens  # noqa: F401
 from .model import (  # noqa: F401
     ar_decode,
     kv_compact_layers,

@@ -65,6 +65,25 @@ def test_m2_rope_invariants():
         assert abs(s1 - s2) < 1e-9
 
 
+def test_m2b_silu_hand_values():
+    """silu(x) = x * logistic(x): the logistic function's known values at
+    0, +-1 and +-2, the far negative tail and the positive
+    saturation, where the correction falls below fp64 spacing (values to
+    40 digits from a decimal evaluation of x / (1 + e^-x))."""
+    x = np.array([0.0, 1.0, -1.0, 2.0, -2.0, -30.0, 40.0])
+    want = np.array([0.0,
+                     0.7310585786300049,      # logistic(1)
+                     -0.2689414213699951,     # -logistic(-1) = -(1 - logistic(1))
+                     1.7615941559557646,      # 2 * logistic(2)
+                     -0.2384058440442351,     # -2 * logistic(-2)
+                     -2.807286890651790e-12,   # -30 / (1 + e^30)
+                     40.0])
+    np.testing.assert_allclose(oracle.silu(x), want, rtol=1e-15, atol=0)
+    # odd part: silu(x) - silu(-x) = x for every x
+    y = np.linspace(-8, 8, 33)
+    np.testing.assert_allclose(oracle.silu(y) - oracle.silu(-y), y, rtol=0, atol=1e-14)
+
+
 def test_m3_node_positions_hand_tree():
     parent = np.array([[-1, 0, 0, 1, 3, 2]])
     np.testing.assert_array_equal(oracle.node_positions(parent, [10]),

@@ -432,6 +432,54 @@ def test_p10_cross_step_invariant():
                 np.testing.assert_allclose(w @ V, tree_out[b, node, h], atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_verify_step_composes_the_pinned_parts(seed):
+    """The whole-step oracle against independent checks of each part's
+    result: the LM head's greedy tokens against a dense argmax of the exact
+    logits, the accepted path and bonus against brute-force enumeration, the
+    emitted chain against the greedy tokens it must follow, the caches
+    against the row moves the path names, and every accepted node's tree
+    output against causal attention over the compacted rows (the cross-step
+    invariant)."""
+    rng = np.random.default_rng(1200 + seed)
+    B, Hkv, G, L, N, D, hid, V = 2, 2, 2, 9, 14, 8, 6, 5
+    Hq = Hkv * G
+    k, v = _caches(rng, B, Hkv, L, N, D)
+    att = dict(q=_rand_f32(rng, (B, N, Hq, D)), k_cache=k, v_cache=v,
+               seq_lens=np.array([L, L - 4], np.int32),
+               parent=np.stack([_random_tree(rng, N) for _ in range(B)]), scale=0.3)
+    lm = dict(hidden=rng.integers(-3, 4, size=(B * N, hid)).astype(np.float32),
+              w=rng.integers(-3, 4, size=(V, hid)).astype(np.float32))
+    # exact small-integer logits: the greedy token is the first maximum
+    logits = lm["hidden"].astype(np.int64) @ lm["w"].astype(np.int64).T
+    tgt = np.array([int(np.flatnonzero(r == r.max())[0]) for r in logits]).reshape(B, N)
+    draft = np.take_along_axis(tgt, np.maximum(att["parent"], 0), axis=1)
+    draft = np.where(rng.random((B, N)) < 0.25, rng.integers(0, V, size=(B, N)), draft)
+    draft = draft.astype(np.int32)
+    res = oracle.verify_step(att, lm, draft, "f32", P=N + 1)
+    np.testing.assert_array_equal(res["tgt"], tgt)
+    for b in range(B):
+        Lb = int(att["seq_lens"][b])
+        path, bonus = _brute_accept(att["parent"][b], draft[b], tgt[b])
+        n = int(res["accept"]["path_len"][b])
+        assert list(res["accept"]["path"][b, :n]) == path
+        assert int(res["accept"]["bonus"][b]) == int(bonus)
+        for j in range(1, n):   # every emitted draft is the greedy token of its parent
+            assert draft[b, path[j]] == tgt[b, path[j - 1]]
+        assert res["seq_lens"][b] == Lb + n
+        for row in range(k.shape[2]):
+            src = Lb + path[row - Lb] if 0 <= row - Lb < n else row
+            np.testing.assert_array_equal(res["k_cache"][b, :, row], k[b, :, src])
+            np.testing.assert_array_equal(res["v_cache"][b, :, row], v[b, :, src])
+        for j, node in enumerate(path):
+            for h in range(Hq):
+                K = res["k_cache"][b, h // G, :Lb + j + 1].astype(np.float64)
+                Vv = res["v_cache"][b, h // G, :Lb + j + 1].astype(np.float64)
+                q = att["q"][b, node, h].astype(np.float64)
+                w = _softmax_rows(0.3 * (K @ q)[None])[0]
+                np.testing.assert_allclose(w @ Vv, res["out"][b, node, h], atol=1e-12)
+
+
 # ---------------------------------------------------------------- paged caches
 
 
