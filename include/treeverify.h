@@ -384,6 +384,9 @@ int tv_graph_destroy(tv_graph* graph);
  *     descending, then shallower, then generation order), numbered by depth
  *     and generation, so parent[i] < i.
  *
+ * This one-launch form serves a draft head whose row depends only on the
+ * depth (every branch gets the same candidates); tv_tree_build_level below
+ * takes one row per frontier node (branch-conditioned).
  * draft_logp   [B][depth][V] fp32 normalised log-probabilities of the draft
  *              head (no NaN)
  * root_tokens  [B] int32: token of node 0 (the last accepted token)
@@ -400,6 +403,52 @@ int tv_tree_build(const float* draft_logp, const int32_t* root_tokens, int B,
                   int depth, int V, int width, int budget, int32_t* parent,
                   int32_t* tokens, int32_t* node_depth, float* score,
                   void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Branch-conditioned tree construction, one level per call.  The JetSpec
+ * abstract describes the draft head as causal and parallel: it conditions
+ * every branch on its own path ("branch-wise causal conditioning"), so that
+ * the tree's scores follow the target's autoregressive factorisation.  The
+ * candidates below a frontier node therefore come from that node's own
+ * row.  The algorithm is the accum_logp reading above with one change: the
+ * candidates of a child of frontier node r at level d are the `width`
+ * largest entries of row r of that level's call, and the child's score is
+ * its parent's score + that row's log-probability of its token.
+ *
+ * Call order, on one stream (or otherwise ordered), with one workspace:
+ * tv_tree_build_level for level = 1, 2, ..., depth, then
+ * tv_tree_build_finish.  Between two level calls the caller runs its draft
+ * head on the paths the previous call reported.
+ *
+ * tv_tree_build_level:
+ *   draft_logp     [B][width][V] fp32 normalised log-probabilities (no NaN);
+ *                  row r of sequence b is the draft head's distribution of
+ *                  the token after the root path of frontier node r (rank
+ *                  order of the previous call's frontier).  Level 1 reads
+ *                  row 0 only (the root's row).
+ *   level          1..depth
+ *   frontier_src   [B][width] int32 (written): for each rank r' of the new
+ *                  frontier (best first), the rank of its parent in the
+ *                  previous frontier (0 at level 1, whose parent is the root)
+ *   frontier_tok   [B][width] int32 (written): the token of that node
+ *   So the path of new frontier node r' is the path of previous node
+ *   frontier_src[b][r'] followed by frontier_tok[b][r'].
+ * tv_tree_build_finish:
+ *   root_tokens, parent, tokens, node_depth, score as for tv_tree_build; the
+ *   root plus the `budget` best candidates of every level's pool.
+ * workspace        tv_tree_build_level_workspace() bytes; it carries the
+ *                  candidate pool and the frontier from call to call (no
+ *                  initial contents needed: level 1 starts a new tree).
+ * Supported: as tv_tree_build.  Rejected calls (TV_EINVAL, TV_ENOTSUP,
+ * TV_EWORKSPACE) enqueue nothing and leave the workspace's tree unchanged.
+ */
+size_t tv_tree_build_level_workspace(int B, int depth, int V, int width);
+int tv_tree_build_level(const float* draft_logp, int level, int B, int depth, int V,
+                        int width, int32_t* frontier_src, int32_t* frontier_tok,
+                        void* workspace, size_t ws_bytes, void* stream);
+int tv_tree_build_finish(const int32_t* root_tokens, int B, int depth, int V, int width,
+                         int budget, int32_t* parent, int32_t* tokens, int32_t* node_depth,
+                         float* score, void* workspace, size_t ws_bytes, void* stream);
 
 /* Text of a status code (TV_EHIP: the HIP error text of the failed launch). */
 const char* tv_status_string(int status);

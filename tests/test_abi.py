@@ -269,6 +269,41 @@ def test_tree_build_host_validation(lib):
     assert call(ws=None) == -3
 
 
+def test_tree_build_level_host_validation(lib):
+    ws = lib.tv_tree_build_level_workspace(1, 20, 151936, 7)
+    assert ws > 0
+    assert lib.tv_tree_build_level_workspace(1, 20, 151936, 17) == 0
+    ok = dict(lp=FAKE, level=1, B=1, D=20, V=151936, W=7, fs=FAKE, ft=FAKE, ws=FAKE, n=ws)
+
+    def lv(**kw):
+        a = dict(ok, **kw)
+        return lib.tv_tree_build_level(a["lp"], a["level"], a["B"], a["D"], a["V"], a["W"],
+                                       a["fs"], a["ft"], a["ws"], a["n"], None)
+    assert lv(lp=None) == -1
+    assert lv(fs=None) == -1
+    assert lv(ft=None) == -1
+    assert lv(level=0) == -1
+    assert lv(level=21) == -1                    # beyond depth
+    assert lv(V=5) == -1                         # V < width
+    assert lv(W=17) == -2
+    assert lv(D=65) == -2
+    assert lv(W=16, D=17) == -2                  # pool above 4096 candidates
+    assert lv(ws=None) == -3
+    assert lv(n=ws - 1) == -3
+
+    def fin(**kw):
+        a = dict(ok, root=FAKE, budget=128, par=FAKE, tok=FAKE)
+        a.update(kw)
+        return lib.tv_tree_build_finish(a["root"], a["B"], a["D"], a["V"], a["W"], a["budget"],
+                                        a["par"], a["tok"], None, None, a["ws"], a["n"], None)
+    assert fin(root=None) == -1
+    assert fin(par=None) == -1
+    assert fin(budget=0) == -1
+    assert fin(W=2, D=2, budget=7) == -1         # budget above the 6 candidates
+    assert fin(W=8, budget=1024) == -2           # budget + 1 > TV_MAX_NODES (pool 1224)
+    assert fin(ws=None) == -3
+
+
 def test_binding_names_match_the_c_calls():
     import tree_draft_verification_amd as tv
     for n in ("tv_tree_verify_attn", "tv_lmhead_argmax", "tv_tree_accept", "tv_kv_compact",
@@ -279,6 +314,7 @@ def test_binding_names_match_the_c_calls():
               "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
               "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_status_string",
-              "tv_abi_version"):
+              "tv_abi_version", "tv_tree_build", "tv_tree_build_workspace",
+              "tv_tree_build_level", "tv_tree_build_level_workspace", "tv_tree_build_finish"):
         assert callable(getattr(tv, n))
     assert tv.tv_status_string(-3) == "workspace missing or too small"

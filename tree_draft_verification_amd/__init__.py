@@ -45,7 +45,8 @@ __all__ = [
     "Model", "tv_model_pack", "tv_verify_pass", "tv_verify_pass_workspace",
     "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "Graph", "tv_graph_begin",
     "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_tree_build",
-    "tv_tree_build_workspace",
+    "tv_tree_build_workspace", "tv_tree_build_level", "tv_tree_build_level_workspace",
+    "tv_tree_build_finish",
 ]
 
 
@@ -575,4 +576,65 @@ def tv_tree_build(draft_logp, root_tokens, width: int, budget: int, *, parent=No
         _ptr(node_depth), _ptr(score), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(dev))
     _check("tv_tree_build", st)
+    return parent, tokens
+
+
+def tv_tree_build_level_workspace(B: int, depth: int, V: int, width: int) -> int:
+    return int(_lib_handle().tv_tree_build_level_workspace(B, depth, V, width))
+
+
+def tv_tree_build_level(draft_logp, level: int, depth: int, *, frontier_src=None,
+                        frontier_tok=None, workspace=None):
+    """One level of a branch-conditioned tree.  draft_logp [B, width, V] fp32:
+    row r is the draft head's row after the path of frontier node r (level 1
+    reads row 0).  Returns (frontier_src, frontier_tok) [B, width] int32.
+    Calls for levels 1..depth and tv_tree_build_finish share one workspace
+    (by default one cached per device: build one tree at a time with it)."""
+    B, W, V = draft_logp.shape
+    if draft_logp.dtype != torch.float32:
+        raise TypeError("draft_logp must be float32")
+    dev = draft_logp.device
+    if frontier_src is None:
+        frontier_src = torch.empty((B, W), dtype=torch.int32, device=dev)
+    if frontier_tok is None:
+        frontier_tok = torch.empty((B, W), dtype=torch.int32, device=dev)
+    _i32(frontier_src, (B, W), "frontier_src")
+    _i32(frontier_tok, (B, W), "frontier_tok")
+    need = tv_tree_build_level_workspace(B, depth, V, W)
+    if workspace is None:
+        workspace = _cached_workspace("tree_level", need, dev)
+    st = _lib_handle().tv_tree_build_level(
+        _ptr(draft_logp), level, B, depth, V, W, _ptr(frontier_src), _ptr(frontier_tok),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("tv_tree_build_level", st)
+    return frontier_src, frontier_tok
+
+
+def tv_tree_build_finish(root_tokens, depth: int, V: int, width: int, budget: int, *,
+                         parent=None, tokens=None, node_depth=None, score=None, workspace=None):
+    """Budget cut and numbering of the tree built by tv_tree_build_level
+    calls.  Returns (parent, tokens) [B, budget+1] int32 (node_depth /
+    score are filled when given)."""
+    B = root_tokens.shape[0]
+    _i32(root_tokens, (B,), "root_tokens")
+    N = budget + 1
+    dev = root_tokens.device
+    if parent is None:
+        parent = torch.empty((B, N), dtype=torch.int32, device=dev)
+    if tokens is None:
+        tokens = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _i32(parent, (B, N), "parent")
+    _i32(tokens, (B, N), "tokens")
+    if node_depth is not None:
+        _i32(node_depth, (B, N), "node_depth")
+    if score is not None and (score.dtype != torch.float32 or tuple(score.shape) != (B, N)):
+        raise ValueError("score must be float32 of shape (B, budget+1)")
+    need = tv_tree_build_level_workspace(B, depth, V, width)
+    if workspace is None:
+        workspace = _cached_workspace("tree_level", need, dev)
+    st = _lib_handle().tv_tree_build_finish(
+        _ptr(root_tokens), B, depth, V, width, budget, _ptr(parent), _ptr(tokens),
+        _ptr(node_depth), _ptr(score), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev))
+    _check("tv_tree_build_finish", st)
     return parent, tokens

@@ -360,4 +360,45 @@ int tv_tree_build(const float* draft_logp, const int32_t* root_tokens, int B, in
                                           static_cast<hipStream_t>(stream)));
 }
 
+
+size_t tv_tree_build_level_workspace(int B, int depth, int V, int width) {
+  if (B < 1 || depth < 1 || V < 1 || width < 1 || width > 16) return 0;
+  return tv::tree_level_ws_bytes(B, depth, V, width);
+}
+
+static int tree_level_shape_ok(int B, int depth, int V, int width) {
+  if (B < 1 || depth < 1 || V < 1 || width < 1 || V < width) return TV_EINVAL;
+  if (width > 16 || depth > 64 || B > 65535) return TV_ENOTSUP;
+  if ((long long)width + (long long)(depth - 1) * width * width > 4096) return TV_ENOTSUP;
+  if ((long long)B * width * V > (1LL << 40)) return TV_ENOTSUP;
+  return TV_OK;
+}
+
+int tv_tree_build_level(const float* draft_logp, int level, int B, int depth, int V, int width,
+                        int32_t* frontier_src, int32_t* frontier_tok, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (!draft_logp || !frontier_src || !frontier_tok) return TV_EINVAL;
+  const int st = tree_level_shape_ok(B, depth, V, width);
+  if (st != TV_OK) return st;
+  if (level < 1 || level > depth) return TV_EINVAL;
+  if (!workspace || ws_bytes < tv::tree_level_ws_bytes(B, depth, V, width)) return TV_EWORKSPACE;
+  return hip_status(tv::launch_tree_level(draft_logp, level, B, depth, V, width, frontier_src,
+                                          frontier_tok, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int tv_tree_build_finish(const int32_t* root_tokens, int B, int depth, int V, int width,
+                         int budget, int32_t* parent, int32_t* tokens, int32_t* node_depth,
+                         float* score, void* workspace, size_t ws_bytes, void* stream) {
+  if (!root_tokens || !parent || !tokens) return TV_EINVAL;
+  const int st = tree_level_shape_ok(B, depth, V, width);
+  if (st != TV_OK) return st;
+  if (budget < 1 || budget > tv::tree_build_pool(depth, width)) return TV_EINVAL;
+  if (budget + 1 > TV_MAX_NODES) return TV_ENOTSUP;
+  if (!workspace || ws_bytes < tv::tree_level_ws_bytes(B, depth, V, width)) return TV_EWORKSPACE;
+  return hip_status(tv::launch_tree_finish(root_tokens, B, depth, V, width, budget, parent, tokens,
+                                           node_depth, score, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

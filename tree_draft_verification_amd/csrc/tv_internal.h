@@ -184,6 +184,13 @@ hipError_t launch_kv_compact_layers(void* k, void* v, int32_t* seq_lens, const i
 
 int tree_build_pool(int depth, int width);  // candidate nodes of a tree
 size_t tree_build_ws_bytes(int B, int depth, int V, int width);
+size_t tree_level_ws_bytes(int B, int depth, int V, int width);
+hipError_t launch_tree_level(const float* logp, int level, int B, int depth, int V, int width,
+                             int32_t* frontier_src, int32_t* frontier_tok, void* ws,
+                             hipStream_t stream);
+hipError_t launch_tree_finish(const int32_t* root_tokens, int B, int depth, int V, int width,
+                              int budget, int32_t* parent, int32_t* tokens, int32_t* node_depth,
+                              float* score, void* ws, hipStream_t stream);
 hipError_t launch_tree_build(const float* logp, const int32_t* root_tokens, int B, int depth,
                              int V, int width, int budget, int32_t* parent, int32_t* tokens,
                              int32_t* node_depth, float* score, void* ws, hipStream_t stream);

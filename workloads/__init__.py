@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     TREE_BUILDS,
     TreeBuildConfig,
     draft_logp,
+    PathDrafter,
     bf16_bits_from_f32,
     BF16_QNAN,
 )

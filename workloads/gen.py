@@ -399,3 +399,35 @@ def draft_logp(cfg: TreeBuildConfig) -> dict:
     logp = (logits - lse).astype(np.float32)
     root = np.random.default_rng(s[1]).integers(0, cfg.V, size=cfg.B).astype(np.int32)
     return dict(logp=logp, root_tokens=root)
+
+
+class PathDrafter:
+    """A synthetic branch-conditioned draft head: the row after a token path
+    (root token first) of sequence b is the log-softmax (fp64, rounded to
+    fp32) of logits ~ N(0, scale^2) drawn from a generator seeded by (seed,
+    b, path), optionally rounded to multiples of `quantum` first (exact
+    ties).  Every branch therefore gets its own distribution, as the JetSpec
+    abstract's causal parallel draft head conditions each branch on its own
+    path.  It stands for the draft head's output, which lies outside tree
+    construction; rows are cached per path."""
+
+    def __init__(self, V: int, seed: int, scale: float = 3.0, quantum: float | None = None):
+        self.V, self.seed, self.scale, self.quantum = V, seed, scale, quantum
+        self._rows: dict = {}
+
+    def row(self, b: int, path) -> np.ndarray:
+        key = (int(b),) + tuple(int(t) for t in path)
+        r = self._rows.get(key)
+        if r is None:
+            rng = np.random.default_rng(np.random.SeedSequence([self.seed, len(key)] + list(key)))
+            x = self.scale * rng.standard_normal(self.V)
+            if self.quantum:
+                x = np.round(x / self.quantum) * self.quantum
+            x = x - x.max()
+            r = (x - np.log(np.exp(x).sum())).astype(np.float32)
+            self._rows[key] = r
+        return r
+
+    def roots(self, B: int) -> np.ndarray:
+        rng = np.random.default_rng(np.random.SeedSequence([self.seed, 0xC0FFEE]))
+        return rng.integers(0, self.V, size=B).astype(np.int32)
