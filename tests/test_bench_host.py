@@ -38,24 +38,31 @@ def test_roof_entry_picks_the_binding_roof():
 
 
 def test_algorithmic_work_of_the_default_workload():
+    """The default line is the largest workload: Qwen3-30B-A3B-shaped
+    attention and LM head, 4 sequences of 1024 nodes on 4096-token prefixes."""
     b = _bench()
     from workloads import WORKLOADS
     wl = WORKLOADS[b.DEFAULT_WORKLOAD]
-    assert (wl.B, wl.N, wl.hidden, wl.V, wl.Hq, wl.Hkv, wl.D) == (1, 64, 4096, 151936, 32, 8, 128)
-    depth = np.arange(64, dtype=np.int32)[None, :] % 20
-    a = {"seq_lens": np.array([1024], np.int32), "depth": depth}
-    path = np.zeros((1, 21), np.int32)
+    assert (wl.B, wl.N, wl.hidden, wl.V, wl.Hq, wl.Hkv, wl.D) == (4, 1024, 2048, 151936, 32, 4, 128)
+    depth = np.tile(np.arange(1024, dtype=np.int32) % 25, (4, 1))
+    a = {"seq_lens": np.full(4, 4096, np.int32), "depth": depth}
+    path = np.full((4, 32), -1, np.int32)
+    path_len = np.array([5, 1, 3, 2], np.int32)
     path[0, :5] = [0, 3, 9, 10, 40]       # 4 of 5 rows move (row i != i)
-    path_len = np.array([5], np.int32)
+    path[1, :1] = [0]                     # none
+    path[2, :3] = [0, 1, 7]               # 1 moves
+    path[3, :2] = [0, 2]                  # 1 moves
     w = b.algorithmic_work(wl, a, path, path_len)
     # LM head: the bf16 vocabulary matrix and hidden states once, one int32 per row
-    assert w["lmhead"] == (151936 * 4096 * 2 + 64 * 4096 * 2 + 4 * 64, 2 * 64 * 4096 * 151936)
-    assert w["lmhead"][0] == 1_245_184_256
-    # attention: prefix K and V once; per node its Q, output and own K/V, and its parent
-    prefix = 2 * 1024 * 8 * 128 * 2
-    per_node = 2 * 32 * 128 * 2 + 2 * 8 * 128 * 2 + 4
-    assert w["attn"][0] == prefix + 64 * per_node
+    M = 4 * 1024
+    assert w["lmhead"] == (151936 * 2048 * 2 + M * 2048 * 2 + 4 * M, 2 * M * 2048 * 151936)
+    assert w["lmhead"] == (639_123_456, 2_549_063_090_176)
+    # attention: prefix K and V once per sequence; per node its Q, output and
+    # own K/V, and its parent
+    prefix = 4 * 2 * 4096 * 4 * 128 * 2
+    per_node = 2 * 32 * 128 * 2 + 2 * 4 * 128 * 2 + 4
+    assert w["attn"][0] == prefix + M * per_node == 109_068_288
     # flops: 4 Hq D per visible key; node i sees the prefix, its ancestors and itself
-    assert w["attn"][1] == 4 * 32 * 128 * int((1024 + depth + 1).sum())
+    assert w["attn"][1] == 4 * 32 * 128 * int((4096 + depth + 1).sum())
     # compaction: K and V rows read and written for each moved row, lengths in and out
-    assert w["compact"][0] == 4 * 4 * 8 * 128 * 2 + 8
+    assert w["compact"][0] == 4 * 6 * 4 * 128 * 2 + 8 * 4

@@ -3,8 +3,10 @@ greedy decoding (fp64 oracle): every sequence of a ragged batch must emit
 exactly the tokens plain autoregressive greedy decoding emits (output
 equivalence, EQSPEC/EXSPEC abstract, arXiv 2510.22876 on the RSS reader
 page; lossless by construction, JetSpec GitHub README, "JetSpec >
-Overview"), with each step's trees built by tv_tree_build, verified by the
-multi-layer pass, accepted and compacted per sequence at its own length."""
+Overview"), with each step's trees built level by level from a
+path-conditioned draft head (tv_tree_build_level / tv_tree_build_finish),
+verified by the multi-layer pass, accepted and compacted per sequence at its
+own length."""
 import numpy as np
 import pytest
 
@@ -18,16 +20,19 @@ pytestmark = pytest.mark.gpu
 GAP_EXEMPT = 5e-2   # a reference choice closer than this may legitimately differ
 
 
-def _drafter_logp(rng, ref_b, e_b, depth, V, hit=0.9, boost=8.0):
-    """Draft-head log-probabilities of one sequence: depth d favours the
-    reference token at emitted index e_b + d - 1 with probability `hit`."""
-    x = rng.standard_normal((depth, V))
-    for d in range(1, depth + 1):
-        i = e_b + d - 1
-        tok = ref_b[i] if (i < len(ref_b) and rng.random() < hit) else rng.integers(0, V)
-        x[d - 1, tok] += boost
-    x -= x.max(axis=1, keepdims=True)
-    return (x - np.log(np.exp(x).sum(axis=1, keepdims=True))).astype(np.float32)
+def _drafter_row(rng, ref_b, e_b, path, V, hit=0.9, boost=8.0):
+    """The simulated draft head's row after `path` (root token first): a
+    frontier node whose drafted tokens follow the reference continuation
+    from emitted index e_b favours the next reference token with probability
+    `hit`; any other node favours a token of its own."""
+    x = rng.standard_normal(V)
+    d = len(path) - 1                      # drafted tokens on the path
+    on_ref = list(path[1:]) == [int(t) for t in ref_b[e_b:e_b + d]]
+    i = e_b + d
+    tok = ref_b[i] if (on_ref and i < len(ref_b) and rng.random() < hit) else rng.integers(0, V)
+    x[tok] += boost
+    x -= x.max()
+    return (x - np.log(np.exp(x).sum())).astype(np.float32)
 
 
 def test_multi_step_ragged_decoding_equals_independent_greedy_decoding():
@@ -62,9 +67,17 @@ def test_multi_step_ragged_decoding_equals_independent_greedy_decoding():
     for s in range(steps):
         cur = lens.cpu().numpy()
         e = cur - L0
-        logp = np.stack([_drafter_logp(rng, ref["tokens"][b], int(e[b]), depth, V)
-                         for b in range(B)])
-        par, tok = tv.tv_tree_build(torch.from_numpy(logp).cuda(), i32_dev(root), width, budget)
+        paths = [[(int(root[b]),)] for b in range(B)]
+        for level in range(1, depth + 1):
+            rows = np.zeros((B, width, V), np.float32)
+            for b in range(B):
+                for r, pth in enumerate(paths[b]):
+                    rows[b, r] = _drafter_row(rng, ref["tokens"][b], int(e[b]), pth, V)
+            fs, ft = tv.tv_tree_build_level(torch.from_numpy(rows).cuda(), level, depth)
+            fs, ft = fs.cpu().numpy(), ft.cpu().numpy()
+            paths = [[paths[b][int(fs[b, r])] + (int(ft[b, r]),) for r in range(width)]
+                     for b in range(B)]
+        par, tok = tv.tv_tree_build_finish(i32_dev(root), depth, V, width, budget)
         st = torch.zeros(B, dtype=torch.int32, device="cuda")
         arg = tv.tv_verify_pass(model, tok, par, lens, kc, vc,
                                 max_seq_len=int(cur.max()), dev_status=st)

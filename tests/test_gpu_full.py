@@ -16,12 +16,15 @@ from _helpers import (LOGITS_REL_L2, assert_argmax_ok, assert_attn_close, i32_de
 pytestmark = pytest.mark.gpu
 
 NAMES = list(WORKLOADS)
-# nodes per sequence whose attention output the oracle recomputes
-ATTN_SAMPLE = {"tiny_fp32": None, "qwen3_8b_L1024_N64": None, "qwen3_8b_L16384_N256": 48,
-               "qwen3_8b_ragged8_N64": 12, "qwen3_30b_a3b_B4_L4096_N1024": 16}
-# hidden-state rows whose logits the oracle recomputes
-LM_SAMPLE = {"tiny_fp32": None, "qwen3_8b_L1024_N64": 8, "qwen3_8b_L16384_N256": 16,
-             "qwen3_8b_ragged8_N64": 16, "qwen3_30b_a3b_B4_L4096_N1024": 16}
+# nodes per sequence whose attention output the oracle recomputes: every node
+# except at 1024 nodes, where one node of every group of 8 (so every 64- or
+# 128-row query block of every (sequence, KV head) holds checked rows)
+ATTN_SAMPLE = {"tiny_fp32": None, "qwen3_8b_L1024_N64": None, "qwen3_8b_L16384_N256": None,
+               "qwen3_8b_ragged8_N64": None, "qwen3_30b_a3b_B4_L4096_N1024": ("groups", 8)}
+# hidden-state rows whose logits the oracle recomputes (with M > 64, two rows
+# of every 256-row tile of the products)
+LM_SAMPLE = {"tiny_fp32": None, "qwen3_8b_L1024_N64": 8, "qwen3_8b_L16384_N256": ("groups", 128),
+             "qwen3_8b_ragged8_N64": ("groups", 128), "qwen3_30b_a3b_B4_L4096_N1024": ("groups", 128)}
 
 _CACHE = {}
 
@@ -38,9 +41,17 @@ def _inputs(name):
 
 
 def _sample(n, k, seed):
-    if k is None or k >= n:
+    """All of 0..n-1 (k None), k random indices with the ends, or one random
+    index of every group of g (k = ("groups", g)) with the ends."""
+    if k is None:
         return np.arange(n)
     rng = np.random.default_rng(seed)
+    if isinstance(k, tuple):
+        g = k[1]
+        pick = [g0 + int(rng.integers(0, min(g, n - g0))) for g0 in range(0, n, g)]
+        return np.unique(np.concatenate([[0, n - 1], pick]))
+    if k >= n:
+        return np.arange(n)
     return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=k - 2, replace=False)]))
 
 
@@ -55,8 +66,12 @@ def _oracle_logits_rows(lm, rows, dtype, chunk=8192):
 
 @pytest.mark.parametrize("name", NAMES)
 def test_full_size_step(name):
-    """The step as the benchmark runs it (packed vocabulary projection for
-    bf16); the row-major layout is checked on the argmax as well."""
+    """The step exactly as the benchmark times it: tree attention, the LM
+    head's argmax (packed vocabulary projection for bf16, no logits), then
+    acceptance and compaction in one launch (tv_accept_compact), all checked
+    against the oracle (acceptance and compaction bit-exact).  A second LM-head
+    call writes the logits for their check and must give the same argmax; the
+    row-major layout is checked on the argmax as well."""
     import torch
     import tree_draft_verification_amd as tv
     wl, a, lm, ref_lm = _inputs(name)
@@ -71,20 +86,25 @@ def test_full_size_step(name):
     st = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
     out = tv.tv_tree_verify_attn(q, k, v, lens, par, max_seq_len=int(a["seq_lens"].max()),
                                  scale=a["scale"], dev_status=st)
-    logits = torch.empty((wl.M, wl.V), dtype=torch.float32, device="cuda")
     w_step = tv.tv_lmhead_pack_weights(w) if wl.dtype == "bf16" else w
-    arg = tv.tv_lmhead_argmax(h, w_step, logits=logits)
-    arg_rm = tv.tv_lmhead_argmax(h, w)
-    path, plen, bonus = tv.tv_tree_accept(par, i32_dev(draft), arg, 32, dev_status=st)
-    tv.tv_kv_compact(k, v, lens, path, plen)
+    arg = tv.tv_lmhead_argmax(h, w_step)
+    path, plen, bonus = tv.tv_accept_compact(par, i32_dev(draft), arg, k, v, lens, 32,
+                                             dev_status=st)
     torch.cuda.synchronize()
     assert st.cpu().numpy().tolist() == [0] * wl.B
+    logits = torch.empty((wl.M, wl.V), dtype=torch.float32, device="cuda")
+    arg_l = tv.tv_lmhead_argmax(h, w_step, logits=logits)
+    arg_rm = tv.tv_lmhead_argmax(h, w)
+    assert torch.equal(arg_l, arg)
 
     # attention: sampled nodes (all of them where cheap)
     nodes = _sample(wl.N, ATTN_SAMPLE[name], wl.seed)
     ref_o = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"],
                                   a["parent"], a["scale"], wl.dtype, nodes=nodes)
-    mx, rel = assert_attn_close(to_host_f64(out), ref_o, name)
+    got_o = to_host_f64(out)
+    mx, rel = assert_attn_close(got_o, ref_o, name)
+    for b in range(wl.B):   # the bound holds sequence by sequence too
+        assert_attn_close(got_o[b], ref_o[b], f"{name} sequence {b}")
     print(f"[full] {name}: attention max|d|={mx:.2e} rel={rel:.2e} on {len(nodes)} nodes/seq",
           flush=True)
 

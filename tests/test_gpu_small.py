@@ -149,14 +149,17 @@ LM_CASES = {
 }
 
 
-@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
-@pytest.mark.parametrize("name", list(LM_CASES))
+# (case, packed layout): the packed layout exists for bf16 only
+LM_LAYOUT_CASES = [(n, p) for n, wl in LM_CASES.items()
+                   for p in ((False, True) if wl.dtype == "bf16" else (False,))]
+
+
+@pytest.mark.parametrize("name,packed", LM_LAYOUT_CASES,
+                         ids=[f"{n}-{'packed' if p else 'rowmajor'}" for n, p in LM_LAYOUT_CASES])
 def test_lmhead_elementwise(name, packed):
     import torch
     import tree_draft_verification_amd as tv
     wl = LM_CASES[name]
-    if packed and wl.dtype != "bf16":
-        pytest.skip("the packed layout is bf16 only")
     lm = lmhead_inputs(wl)
     M, V = wl.M, wl.V
     print(f"[lmhead] {name} M={M} K={wl.hidden} V={V}", flush=True)
@@ -235,6 +238,49 @@ def test_lmhead_ties_go_to_smallest_index():
     for wt in (wd, tv.tv_lmhead_pack_weights(wd)):
         arg = tv.tv_lmhead_argmax(to_dev(h, "bf16"), wt).cpu().numpy()
         np.testing.assert_array_equal(arg, np.argmax(exact, axis=1))
+
+
+def test_lmhead_stream_kernel_ties_across_its_tiles():
+    """Up to 64 rows the persistent kernel walks 128-row vocabulary tiles
+    b, b + grid, ...; duplicate W rows farther apart than one grid's worth
+    of tiles tie across the tiles one workgroup walks and across workgroups:
+    the smallest index wins."""
+    import tree_draft_verification_amd as tv
+    from workloads import bf16_bits_from_f32
+    rng = np.random.default_rng(38)
+    M, K, V = 17, 256, 150000
+    Hi = rng.integers(1, 3, size=(M, K)).astype(np.float32)     # positive
+    Wi = rng.integers(-1, 2, size=(V, K)).astype(np.float32)
+    # all-ones rows score sum(H[m]), above every random row: exact ties at
+    # the maximum, in tiles 5 and 5 + 768 (one workgroup's first and second
+    # tile with a resident grid of 768), and farther apart than any grid of
+    # at most 1024 tiles
+    dup = [98947, 643, 131079, 140001, 65539]
+    Wi[dup] = 1.0
+    h = bf16_bits_from_f32(Hi)
+    w = bf16_bits_from_f32(Wi)
+    exact = Hi.astype(np.int64) @ Wi.T.astype(np.int64)
+    want = np.argmax(exact, axis=1)
+    assert (want == min(dup)).all()
+    wd = to_dev(w, "bf16")
+    for wt in (wd, tv.tv_lmhead_pack_weights(wd)):
+        arg = tv.tv_lmhead_argmax(to_dev(h, "bf16"), wt).cpu().numpy()
+        np.testing.assert_array_equal(arg, want)
+
+
+def test_lmhead_cached_workspaces_of_mixed_dtypes_and_sizes():
+    """The binding's own workspaces: a bf16 call with M > 64 (which leaves
+    partial keys behind), then fp32 calls with more rows, then the bf16 call
+    again, each equal to the oracle."""
+    import tree_draft_verification_amd as tv
+    for wl in (Q8.replace(B=1, N=100, hidden=256, V=3001, seed=61),
+               Q8.replace(B=1, N=200, hidden=96, V=3001, dtype="f32", seed=62),
+               Q8.replace(B=1, N=300, hidden=96, V=2000, dtype="f32", seed=63),
+               Q8.replace(B=1, N=100, hidden=256, V=3001, seed=61)):
+        lm = lmhead_inputs(wl)
+        arg = tv.tv_lmhead_argmax(to_dev(lm["hidden"], wl.dtype), to_dev(lm["w"], wl.dtype))
+        ref = oracle.lm_head_argmax(lm["hidden"], lm["w"], wl.dtype)
+        assert_argmax_ok(arg.cpu().numpy(), ref, f"M={wl.M} {wl.dtype}")
 
 
 # ---------------------------------------------------------------- accept + compact
@@ -616,3 +662,25 @@ def test_accept_compact_equals_the_two_calls(name):
         for x, y in ((ref_k, got_k), (ref_v, got_v)):  # caches bit for bit
             assert np.array_equal(x.cpu().view(torch.int16 if wl.dtype == "bf16" else torch.int32),
                                   y.cpu().view(torch.int16 if wl.dtype == "bf16" else torch.int32))
+        # and against the oracle, on every sequence the call did not flag
+        # (a flagged sequence's outputs are unspecified)
+        st_h = st_got.cpu().numpy()
+        gk, gv = to_host_bits(got_k), to_host_bits(got_v)
+        p_h, l_h, b_h, len_h = (t.cpu().numpy() for t in (p2, l2, b2, got_l))
+        checked = 0
+        for b in range(wl.B):
+            if st_h[b]:
+                continue
+            acc = oracle.tree_accept(parent[b:b + 1], draft[b:b + 1], tgt[b:b + 1], 64)
+            n = int(acc["path_len"][0])
+            assert l_h[b] == n and b_h[b] == acc["bonus"][0], (name, b)
+            np.testing.assert_array_equal(p_h[b], acc["path"][0, :P])
+            k2, v2, lens2 = oracle.kv_compact(a["k_cache"][b:b + 1], a["v_cache"][b:b + 1],
+                                              a["seq_lens"][b:b + 1], acc["path"],
+                                              acc["path_len"])
+            assert len_h[b] == lens2[0]
+            np.testing.assert_array_equal(gk[b], k2[0])
+            np.testing.assert_array_equal(gv[b], v2[0])
+            checked += 1
+        if P == 32:
+            assert checked >= max(1, wl.B - 1), name

@@ -104,17 +104,23 @@ def _i32(t: torch.Tensor, shape, name: str):
 _WS_CACHE: dict = {}
 
 
-def _cached_workspace(kind: str, nbytes: int, dev: torch.device) -> torch.Tensor:
+def _cached_workspace(kind, nbytes: int, dev: torch.device) -> torch.Tensor:
     """Zero-initialised device scratch reused across calls (grown on demand).
 
-    Calls that share it must be ordered on one stream; the LM-head call
-    returns its part to zero when it completes.
+    Calls that share it must be ordered on one stream.  `kind` names what
+    may share a buffer: LM-head buffers are kept per (dtype, M, K, V), since
+    a call leaves only the part its own shape uses zeroed (at most eight such
+    buffers are kept; the least recently used goes first).
     """
     key = (kind, dev)
-    buf = _WS_CACHE.get(key)
+    buf = _WS_CACHE.pop(key, None)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        _WS_CACHE[key] = buf
+    _WS_CACHE[key] = buf                      # most recently used last
+    if isinstance(kind, tuple):
+        same = [k for k in _WS_CACHE if isinstance(k[0], tuple) and k[0][0] == kind[0]]
+        for k in same[:-8]:
+            del _WS_CACHE[k]
     return buf
 
 
@@ -273,7 +279,7 @@ def tv_lmhead_argmax(hidden, w, argmax=None, logits=None, *,
         raise ValueError("logits must be float32 of shape (M, V)")
     need = tv_lmhead_argmax_workspace(M, K, V, dt)
     if workspace is None:
-        workspace = _cached_workspace("lmhead", need, hidden.device)
+        workspace = _cached_workspace(("lmhead", dt, M, K, V), need, hidden.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = _lib_handle().tv_lmhead_argmax(_ptr(hidden), wptr, _ptr(argmax), _ptr(logits), M, K, V, dt,
                                layout, _ptr(workspace), ws_bytes, _stream(hidden.device))
