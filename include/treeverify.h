@@ -46,6 +46,10 @@ extern "C" {
 #define TV_ENOTSUP    -2 /* valid but unsupported: head dim, dtype, N, ...   */
 #define TV_EWORKSPACE -3 /* workspace null or smaller than the query result  */
 #define TV_EHIP       -4 /* a HIP launch failed                              */
+#define TV_ESCRATCH   -5 /* larger than the allocation-free call's scratch   */
+
+/* Bytes of the device array behind tv_lmhead_argmax_noalloc (per device). */
+#define TV_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 #define TV_BF16 0
 #define TV_F32  1
@@ -153,6 +157,24 @@ int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax,
                      float* logits, int M, int K, int V, int dtype,
                      int w_layout, void* workspace, size_t ws_bytes,
                      void* stream);
+
+/*
+ * tv_lmhead_argmax without a workspace, for callers that cannot allocate
+ * device memory: code under stream capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments, results and checks as for
+ * tv_lmhead_argmax; the same kernels run.  Their scratch is one device array
+ * of TV_NOALLOC_SCRATCH_BYTES per device, held from first use until the
+ * process ends: a shape whose tv_lmhead_argmax_workspace() exceeds it
+ * returns TV_ESCRATCH with nothing enqueued (64 MiB covers 4096 rows at
+ * V = 151936, K = 2048).  The call allocates nothing.  Each call clears the
+ * part that must start at zero, on `stream`, before its kernels; every call
+ * on a device shares that device's array, so calls that may overlap on one
+ * device (other streams, other threads) race and must be ordered by the
+ * caller.
+ */
+int tv_lmhead_argmax_noalloc(const void* hidden, const void* w, int32_t* argmax,
+                             float* logits, int M, int K, int V, int dtype, int w_layout,
+                             void* stream);
 
 /*
  * Repack a row-major bf16 vocabulary projection [V][K] into the layout the

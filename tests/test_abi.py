@@ -113,6 +113,24 @@ def test_lmhead_host_validation(lib):
     assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, 0, FAKE, ws - 1, None) == -3
 
 
+def test_lmhead_noalloc_host_validation(lib):
+    """The allocation-free LM head checks its arguments as the workspace
+    call does, and rejects shapes beyond its device array before any HIP
+    call (TV_ESCRATCH)."""
+    from tree_draft_verification_amd import _lib
+    f = lib.tv_lmhead_argmax_noalloc
+    assert f(None, FAKE, FAKE, None, 64, 4096, 151936, 0, 1, None) == -1
+    assert f(FAKE, FAKE, None, None, 64, 4096, 151936, 0, 1, None) == -1
+    assert f(FAKE, FAKE, FAKE, None, 0, 4096, 151936, 0, 1, None) == -1
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 0, 7, None) == -1   # layout
+    assert f(FAKE, FAKE, FAKE, None, 64, 100, 151936, 0, 1, None) == -2    # K % 256
+    assert f(FAKE, FAKE, FAKE, None, 64, 4096, 151936, 1, 1, None) == -2   # f32 packed
+    assert f(FAKE, FAKE, FAKE, None, 8192, 2048, 151936, 0, 1, None) == _lib.TV_ESCRATCH
+    assert lib.tv_lmhead_argmax_workspace(8192, 2048, 151936, 0) > _lib.TV_NOALLOC_SCRATCH_BYTES
+    assert lib.tv_lmhead_argmax_workspace(4096, 2048, 151936, 0) <= _lib.TV_NOALLOC_SCRATCH_BYTES
+    assert b"allocation-free" in lib.tv_status_string(_lib.TV_ESCRATCH)
+
+
 def test_pack_host_validation(lib):
     assert lib.tv_lmhead_packed_bytes(151936, 4096, 0) == 151936 * 4096 * 2
     assert lib.tv_lmhead_packed_bytes(1000, 256, 0) == 1024 * 256 * 2      # whole 128-row tiles

@@ -6,7 +6,8 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libtreeverify.so")
 
-TV_OK, TV_EINVAL, TV_ENOTSUP, TV_EWORKSPACE, TV_EHIP = 0, -1, -2, -3, -4
+TV_OK, TV_EINVAL, TV_ENOTSUP, TV_EWORKSPACE, TV_EHIP, TV_ESCRATCH = 0, -1, -2, -3, -4, -5
+TV_NOALLOC_SCRATCH_BYTES = 64 << 20
 TV_BF16, TV_F32 = 0, 1
 TV_LAYOUT_ROWMAJOR, TV_LAYOUT_PACKED = 0, 1
 TV_STATUS_BAD_PARENT, TV_STATUS_BAD_LEN, TV_STATUS_DEPTH, TV_STATUS_BAD_PAGE = 1, 2, 4, 8
@@ -44,6 +45,7 @@ SIGNATURES = {
     "tv_kv_compact_paged": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "tv_lmhead_argmax_workspace": (_sz, [_i, _i, _i, _i]),
     "tv_lmhead_argmax": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
+    "tv_lmhead_argmax_noalloc": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
     "tv_lmhead_packed_bytes": (_sz, [_i, _i, _i]),
     "tv_lmhead_pack_weights": (_i, [_p, _p, _i, _i, _i, _p]),
     "tv_pack_gate_up_weights": (_i, [_p, _p, _i, _i, _i, _p]),

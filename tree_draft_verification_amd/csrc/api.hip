@@ -10,6 +10,12 @@ namespace {
 
 thread_local char g_hip_msg[256];
 
+bool dtype_ok(int dtype) { return dtype == TV_BF16 || dtype == TV_F32; }
+
+}  // namespace
+
+namespace tv {
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return TV_OK;
   snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP launch failed: %s (%d)", hipGetErrorString(e),
@@ -17,9 +23,24 @@ int hip_status(hipError_t e) {
   return TV_EHIP;
 }
 
-bool dtype_ok(int dtype) { return dtype == TV_BF16 || dtype == TV_F32; }
+int lmhead_check(const void* hidden, const void* w, const int32_t* argmax, int M, int K, int V,
+                 int dtype, int w_layout) {
+  if (!hidden || !w || !argmax) return TV_EINVAL;
+  if (M < 1 || K < 1 || V < 1) return TV_EINVAL;
+  if (w_layout != TV_LAYOUT_ROWMAJOR && w_layout != TV_LAYOUT_PACKED) return TV_EINVAL;
+  if (!dtype_ok(dtype)) return TV_ENOTSUP;
+  if (dtype == TV_BF16 && K % 256) return TV_ENOTSUP;
+  if (dtype == TV_F32 && w_layout != TV_LAYOUT_ROWMAJOR) return TV_ENOTSUP;
+  const long long blocks = dtype == TV_BF16
+                               ? (long long)((M + 63) / 64) * ((V + 127) / 128)
+                               : (long long)((M + 15) / 16) * ((V + 255) / 256);
+  if (blocks > 2147483647LL) return TV_ENOTSUP;
+  return TV_OK;
+}
 
-}  // namespace
+}  // namespace tv
+
+using tv::hip_status;
 
 extern "C" {
 
@@ -32,6 +53,8 @@ const char* tv_status_string(int status) {
     case TV_ENOTSUP: return "unsupported configuration (head dim, dtype, layout, node count or width)";
     case TV_EWORKSPACE: return "workspace missing or too small";
     case TV_EHIP: return g_hip_msg[0] ? g_hip_msg : "HIP launch failed";
+    case TV_ESCRATCH:
+      return "problem larger than the static scratch of the allocation-free call";
     default: return "unknown status";
   }
 }
@@ -152,16 +175,8 @@ int tv_pack_gate_up_weights(const void* w, void* w_packed, int inter, int K, int
 int tv_lmhead_argmax(const void* hidden, const void* w, int32_t* argmax, float* logits, int M,
                      int K, int V, int dtype, int w_layout, void* workspace, size_t ws_bytes,
                      void* stream) {
-  if (!hidden || !w || !argmax) return TV_EINVAL;
-  if (M < 1 || K < 1 || V < 1) return TV_EINVAL;
-  if (w_layout != TV_LAYOUT_ROWMAJOR && w_layout != TV_LAYOUT_PACKED) return TV_EINVAL;
-  if (!dtype_ok(dtype)) return TV_ENOTSUP;
-  if (dtype == TV_BF16 && K % 256) return TV_ENOTSUP;
-  if (dtype == TV_F32 && w_layout != TV_LAYOUT_ROWMAJOR) return TV_ENOTSUP;
-  const long long blocks = dtype == TV_BF16
-                               ? (long long)((M + 63) / 64) * ((V + 127) / 128)
-                               : (long long)((M + 15) / 16) * ((V + 255) / 256);
-  if (blocks > 2147483647LL) return TV_ENOTSUP;
+  const int st = tv::lmhead_check(hidden, w, argmax, M, K, V, dtype, w_layout);
+  if (st != TV_OK) return st;
   if (!workspace || ws_bytes < tv::lmhead_ws_bytes(M, K, V, dtype)) return TV_EWORKSPACE;
   return hip_status(tv::launch_lmhead_argmax(hidden, w, argmax, logits, M, K, V, dtype, w_layout,
                                              workspace, ws_bytes,

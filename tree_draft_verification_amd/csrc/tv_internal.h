@@ -102,6 +102,11 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
                             int max_blocks = 0, int page_size = 0, int num_pages = 0);
 
 size_t lmhead_ws_bytes(int M, int K, int V, int dtype);
+// Host checks of tv_lmhead_argmax's arguments other than the workspace.
+int lmhead_check(const void* hidden, const void* w, const int32_t* argmax, int M, int K, int V,
+                 int dtype, int w_layout);
+// TV_OK, or TV_EHIP with the error's text kept for tv_status_string.
+int hip_status(hipError_t e);
 size_t lmhead_packed_bytes(int V, int K);
 
 hipError_t launch_lmhead_pack(const void* w, void* packed, int V, int K, hipStream_t stream);
