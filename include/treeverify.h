@@ -30,6 +30,13 @@
  *     outputs of such a sequence are then unspecified.
  *   - Calls that share a workspace, or that write the same cache, must not
  *     overlap in time (same stream, or ordered by events).
+ *
+ * Two arguments go beyond the bare problem statement, on purpose: the
+ * workspace queries take `dtype` (the fp32 kernels tile differently and need
+ * other scratch than the bf16 ones), and tv_lmhead_argmax takes `w_layout`
+ * (the vocabulary projection is a static weight, repacked once into the
+ * layout the matrix-core kernels stream fastest; the row-major layout stays
+ * accepted).
  */
 #ifndef TREEVERIFY_H
 #define TREEVERIFY_H
@@ -87,7 +94,12 @@ extern "C" {
  *               prefix across workgroups); needs max_seq_len + N <= Lcap
  * scale         softmax scale, normally 1/sqrt(D)
  * workspace     device scratch of at least tv_tree_verify_attn_workspace()
- *               bytes for the same shapes (may be NULL when that is 0)
+ *               bytes for the same shapes (may be NULL when that is 0); no
+ *               initial contents needed.  Long prefixes are split across
+ *               workgroups; for a batch of 2..64 sequences the splits are
+ *               derived on the device from seq_lens (one chunk length for
+ *               the batch), so the workspace covers any lengths up to
+ *               max_seq_len.
  * Supported: D in {64, 128}, 1 <= N <= TV_MAX_NODES, Hq % Hkv == 0.
  * Device-side checks: TV_STATUS_BAD_PARENT, TV_STATUS_BAD_LEN.
  */

@@ -40,6 +40,15 @@ ATTN_CASES = {
     # one query head per KV head: a 128-row block spans 128 nodes, whose
     # ancestor words (3 per node) fill the most dynamic LDS
     "g1_L2100_N130": Q8.replace(Hq=4, Hkv=4, L_lo=2100, L_hi=2100, N=130, seed=24),
+    # ragged batches whose splits come from the lengths on the device: empty
+    # to 3000-token prefixes; the most sequences that path takes (64) with
+    # 64-row blocks; one more (65) on the uniform split
+    "q8_ragged8_L0_3000_N64": WORKLOADS["qwen3_8b_ragged8_N64"].replace(L_lo=0, L_hi=3000,
+                                                                        seed=25),
+    "q8_ragged64_L0_700_N16": WORKLOADS["qwen3_8b_ragged8_N64"].replace(
+        B=64, N=16, Hq=8, Hkv=2, L_lo=0, L_hi=700, seed=26),
+    "q8_ragged65_L100_900_N8": WORKLOADS["qwen3_8b_ragged8_N64"].replace(
+        B=65, N=8, Hq=4, Hkv=1, L_lo=100, L_hi=900, seed=27),
 }
 
 
@@ -121,6 +130,29 @@ def test_attention_flags_bad_trees_and_lengths():
     tv.tv_tree_verify_attn(q, k, v, i32_dev(lens), i32_dev(a["parent"]),
                            max_seq_len=100, dev_status=st)
     assert st.cpu().tolist() == [tv.TV_STATUS_BAD_LEN, 0]
+
+
+def test_attention_ragged_batch_flags_one_bad_length():
+    """A ragged batch (splits derived from the lengths on the device) with
+    one length above max_seq_len: that sequence is flagged and counts as no
+    prefix in the plan; the others equal the oracle."""
+    import torch
+    import tree_draft_verification_amd as tv
+    wl = WORKLOADS["qwen3_8b_ragged8_N64"].replace(B=4, L_lo=1500, L_hi=2500, seed=29)
+    a = attn_inputs(wl)
+    msl = int(a["seq_lens"].max())
+    lens = a["seq_lens"].copy()
+    lens[2] = msl + 1
+    st = torch.zeros(wl.B, dtype=torch.int32, device="cuda")
+    q, k, v = (to_dev(a[x], "bf16") for x in ("q", "k_cache", "v_cache"))
+    out = tv.tv_tree_verify_attn(q, k, v, i32_dev(lens), i32_dev(a["parent"]),
+                                 max_seq_len=msl, scale=a["scale"], dev_status=st)
+    assert st.cpu().tolist() == [0, 0, tv.TV_STATUS_BAD_LEN, 0]
+    ref = oracle.tree_attention(a["q"], a["k_cache"], a["v_cache"], a["seq_lens"],
+                                a["parent"], a["scale"], wl.dtype)
+    got = to_host_f64(out)
+    for b in (0, 1, 3):
+        assert_attn_close(got[b], ref[b], f"sequence {b}")
 
 
 def test_attention_deterministic():
@@ -458,7 +490,13 @@ PAGED_CASES = {
     "g1_L64_N130_ps128": ("g1_L64_N130", 128),
     "q8_ragged2_L2000_3100_N64_ps16": ("q8_ragged2_L2000_3100_N64", 16),
     "g1_L2100_N130_ps64": ("g1_L2100_N130", 64),
+    "q8_ragged8_L0_3000_N64_ps16": ("q8_ragged8_L0_3000_N64", 16),
+    # 16-row pages and prefixes past 510 tiles: a split's block-table entries
+    # cap the chunk length of the ragged plan
+    "ragged2_L33500_36000_N16_ps16": ("ragged2_L33500_36000_N16", 16),
 }
+ATTN_CASES["ragged2_L33500_36000_N16"] = WORKLOADS["qwen3_8b_ragged8_N64"].replace(
+    B=2, N=16, Hq=2, Hkv=1, L_lo=33500, L_hi=36000, seed=28)
 
 
 def _paged_dev(pg, dtype):

@@ -68,12 +68,16 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* parent;
   bf16_t* out;
-  float* part_o;   // [B*Hkv][nqblk*rows][nsplit][D] fp32
-  float* part_ml;  // [B*Hkv][nqblk*rows][nsplit][2] fp32
+  float* part_o;   // [B*Hkv][nqblk*rows][nsplit][D] fp32 (ragged: [item][Hkv][nqblk*rows][D])
+  float* part_ml;  // [B*Hkv][nqblk*rows][nsplit][2] fp32 (ragged: [item][Hkv][nqblk*rows][2])
   int32_t* dev_status;
   int B, N, Hq, Hkv, G, Lcap, max_seq_len;
   int rows;        // query rows per workgroup
   int nqblk, nsplit, chunk_len, total_blocks;
+  // ragged batches: per-sequence splits derived on the device from the
+  // lengths (ragged_plan); nsplit and chunk_len above are then unused
+  int ragged, want_blocks, min_tiles, max_chunk_tiles;
+  int* ragged_start;  // [B + 1] (ragged): workgroup 0 publishes the plan here for the combine
   int anc_words;   // ceil(N / 64)
   float scale_log2;  // scale * log2(e)
   // paged caches (block_table != nullptr): pools [num_pages][Hkv][ps][D],
@@ -107,6 +111,81 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// Prefix splits of a ragged batch (at most kMaxRaggedB sequences), derived
+// from the lengths so that every split holds about the same number of key
+// tiles whatever the mix of lengths: chunk = max(min_tiles, ceil(total tiles
+// x Hkv x query blocks / want_blocks)) tiles (at most max_chunk_tiles),
+// nsplit_b = max(1, ceil(tiles_b / chunk)), and every sequence with more
+// than one split gets one more for its tree keys while the whole grid stays
+// within want_blocks.  Work items (b, split) are numbered sequence by
+// sequence; start[b] is the first item of sequence b, start[B] the count.
+// Every workgroup of a launch derives the same plan (wavefront 0 computes it,
+// one sequence per lane; a barrier publishes it).  A length outside
+// [0, max_seq_len] counts as no prefix (its workgroups flag it and return).
+constexpr int kMaxRaggedB = kMaxRaggedBatch;
+
+struct RaggedPlan {
+  const int* start;  // [B + 1], in LDS
+  int chunk_len;     // keys per prefix split
+};
+
+__device__ RaggedPlan ragged_plan(const AttnArgs& a) {
+  __shared__ int sStart[kMaxRaggedB + 1];
+  __shared__ int sChunk;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int lane = tid;
+    int tiles = 0;
+    if (lane < a.B) {
+      const int L = a.seq_lens[lane];
+      tiles = (L >= 0 && L <= a.max_seq_len) ? (L + kKT - 1) / kKT : 0;
+    }
+    int total = tiles, most = tiles;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      total += __shfl_xor(total, off, 64);
+      most = max(most, __shfl_xor(most, off, 64));
+    }
+    const long hq = (long)a.Hkv * a.nqblk;
+    auto items_at = [&](long c) {  // work items of the batch with chunks of c tiles
+      int n = lane < a.B ? max(1, (int)((tiles + c - 1) / c)) : 0;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off, 64);
+      return (long)n;
+    };
+    // the smallest chunk (at least the even share, min_tiles and at most
+    // max_chunk_tiles) whose items fit the workgroup target: the per-sequence
+    // rounding up must not push the grid into a second round
+    long ct = ((long)total * hq + a.want_blocks - 1) / a.want_blocks;
+    if (ct < a.min_tiles) ct = a.min_tiles;
+    long hi = most > ct ? most : ct;
+    if (hi > a.max_chunk_tiles) hi = a.max_chunk_tiles;
+    if (ct > hi) ct = hi;
+    while (ct < hi && items_at(ct) * hq > a.want_blocks) {  // non-increasing in ct
+      const long mid = (ct + hi) / 2;
+      if (items_at(mid) * hq <= a.want_blocks) hi = mid;
+      else ct = mid + 1;
+    }
+    int ns = lane < a.B ? max(1, (int)((tiles + ct - 1) / ct)) : 0;
+    const int with_tree = ns + (ns > 1 ? 1 : 0);
+    int sum_tree = with_tree;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum_tree += __shfl_xor(sum_tree, off, 64);
+    if ((long)sum_tree * hq <= a.want_blocks) ns = with_tree;
+    int incl = ns;  // inclusive scan over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane < a.B) sStart[lane] = incl - ns;
+    if (lane == a.B - 1) sStart[a.B] = incl;
+    if (lane == 0) sChunk = (int)ct * kKT;
+  }
+  __syncthreads();
+  return RaggedPlan{sStart, sChunk};
 }
 
 template <int D, int QBW, int NW, bool PAGED>
@@ -149,13 +228,36 @@ void attn_bf16_kernel(AttnArgs a) {
   const int kg = lane >> 4;
 
   // ---- which (sequence, KV head, split, query block) this workgroup owns
-  int t = xcd_remap(blockIdx.x, a.total_blocks);
-  const int qblk = t % a.nqblk;
-  t /= a.nqblk;
-  const int split = t % a.nsplit;
-  t /= a.nsplit;
-  const int g = t % a.Hkv;
-  const int b = t / a.Hkv;
+  int t, qblk, b, g, split, nsplit, chunk_len, item = 0;
+  if (a.ragged) {
+    // the grid covers the most items any lengths can give; the first
+    // `active` workgroup ids (dealt round-robin to the dies) do the work, and
+    // the remap over that count keeps each die's share contiguous
+    const RaggedPlan rp = ragged_plan(a);
+    if (blockIdx.x == 0 && tid <= a.B) a.ragged_start[tid] = rp.start[tid];
+    const int active = rp.start[a.B] * a.Hkv * a.nqblk;
+    if ((int)blockIdx.x >= active) return;
+    t = xcd_remap(blockIdx.x, active);
+    qblk = t % a.nqblk;
+    t /= a.nqblk;
+    g = t % a.Hkv;
+    item = t / a.Hkv;
+    b = 0;
+    while (b + 1 < a.B && rp.start[b + 1] <= item) ++b;
+    split = item - rp.start[b];
+    nsplit = rp.start[b + 1] - rp.start[b];
+    chunk_len = rp.chunk_len;
+  } else {
+    t = xcd_remap(blockIdx.x, a.total_blocks);
+    qblk = t % a.nqblk;
+    t /= a.nqblk;
+    split = t % a.nsplit;
+    t /= a.nsplit;
+    g = t % a.Hkv;
+    b = t / a.Hkv;
+    nsplit = a.nsplit;
+    chunk_len = a.chunk_len;
+  }
 
   const int N = a.N, G = a.G;
   const int R = N * G;
@@ -167,9 +269,9 @@ void attn_bf16_kernel(AttnArgs a) {
   const int row0 = qblk * kRows;
   const int node_lo = row0 / G;
   const int node_hi = (min(R, row0 + kRows) - 1) / G;
-  const bool do_tree = (split == a.nsplit - 1);
-  const int c0 = split * a.chunk_len;
-  const int c1 = min(c0 + a.chunk_len, L);
+  const bool do_tree = (split == nsplit - 1);
+  const int c0 = split * chunk_len;
+  const int c1 = min(c0 + chunk_len, L);
   const int W = a.anc_words;
 
   // ---- ancestor words of the block's nodes and the tree tiles they touch
@@ -556,7 +658,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const float l_tot = sum_across_groups(l_run[qb]);
     if (!qvalid[qb]) continue;
     const int row = row0 + wave * QBW * 16 + qb * 16 + l16;
-    if (a.nsplit == 1) {
+    if (nsplit == 1) {
       const int node = qnode[qb];
       const int hh = row - node * G;
       bf16_t* orow = a.out + (((size_t)b * N + node) * a.Hq + (size_t)g * G + hh) * D;
@@ -570,7 +672,8 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     } else {
       const size_t prow =
-          (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * kRows) + row) * a.nsplit + split;
+          a.ragged ? ((size_t)item * a.Hkv + g) * ((size_t)a.nqblk * kRows) + row
+                   : (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * kRows) + row) * a.nsplit + split;
       float* po = a.part_o + prow * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -584,6 +687,9 @@ void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Merge split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Ragged batches: sequence b's partials are items start[b] .. start[b+1]-1
+// (the plan the attention kernel published); a sequence with one split wrote
+// its output directly.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int D4 = D / 4;
@@ -597,16 +703,28 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   t /= R;
   const int g = (int)(t % a.Hkv);
   const int b = (int)(t / a.Hkv);
-  const size_t prow0 = (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * a.rows) + row) * a.nsplit;
+  int ns = a.nsplit;
+  size_t prow0, pstride;
+  if (a.ragged) {
+    const int s0 = a.ragged_start[b];
+    ns = a.ragged_start[b + 1] - s0;
+    if (ns == 1) return;
+    pstride = (size_t)a.Hkv * a.nqblk * a.rows;
+    prow0 = ((size_t)s0 * a.Hkv + g) * ((size_t)a.nqblk * a.rows) + row;
+  } else {
+    pstride = 1;
+    prow0 = (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * a.rows) + row) * a.nsplit;
+  }
   float mx = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mx = fmaxf(mx, a.part_ml[(prow0 + s) * 2]);
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[(prow0 + s * pstride) * 2]);
   const float m_use = (mx == -INFINITY) ? 0.f : mx;
   float lsum = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[(prow0 + s) * 2] - m_use);
-    lsum += w * a.part_ml[(prow0 + s) * 2 + 1];
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + (prow0 + s) * D + d4 * 4);
+  for (int s = 0; s < ns; ++s) {
+    const size_t pr = prow0 + s * pstride;
+    const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - m_use);
+    lsum += w * a.part_ml[pr * 2 + 1];
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + pr * D + d4 * 4);
     acc += w * v;
   }
   const float inv = 1.f / lsum;
@@ -781,8 +899,36 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dt
   if (dtype == TV_BF16 && p.nsplit > 1 &&
       (long)B * Hkv * p.nqblk * (p.nsplit + 1) <= want_blocks)
     p.nsplit += 1;
+  // A batch of several sequences whose prefixes want splitting takes its
+  // splits from the actual lengths on the device (ragged_plan in the
+  // kernels): one chunk length for the whole batch, so a long sequence gets
+  // many splits and a short one few, instead of every sequence getting the
+  // longest one's split count.  The grid covers the most work items any
+  // lengths up to max_seq_len can give; workgroups past the actual count
+  // return at once.
+  p.ragged = 0;
+  if (dtype == TV_BF16 && B > 1 && B <= kMaxRaggedBatch && p.nsplit > 1) {
+    const long hq = (long)Hkv * p.nqblk;
+    p.ragged = 1;
+    p.want_blocks = (int)want_blocks;
+    p.min_tiles = min_tiles;
+    p.max_chunk_tiles = 1 << 30;
+    long max_items = want_blocks / hq + 1 + 2L * B;
+    if (page_size > 0) {
+      const int tree_blk = N / page_size + 2;
+      const long max_rows = (long)(kMaxPagedBlocks - tree_blk - 2) * page_size;
+      const long max_tiles = max_rows / kKT > 0 ? max_rows / kKT : 1;
+      p.max_chunk_tiles = (int)(max_tiles < (1 << 30) ? max_tiles : (1 << 30));
+      max_items += (long)B * ((ntiles + max_tiles - 1) / max_tiles);
+    }
+    p.max_items = (int)max_items;
+  }
   p.ws_bytes = 0;
-  if (p.nsplit > 1) {
+  if (p.ragged) {
+    const size_t rows = (size_t)p.max_items * Hkv * p.nqblk * p.rows;
+    p.ws_bytes = rows * D * sizeof(float) + rows * 2 * sizeof(float) +
+                 (kMaxRaggedBatch + 1) * sizeof(int);
+  } else if (p.nsplit > 1) {
     const size_t rows = (size_t)B * Hkv * p.nqblk * p.rows * p.nsplit;
     p.ws_bytes = rows * D * sizeof(float) + rows * 2 * sizeof(float);
   }
@@ -823,7 +969,12 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
   a.nqblk = plan.nqblk;
   a.nsplit = plan.nsplit;
   a.chunk_len = plan.chunk_len;
-  a.total_blocks = B * Hkv * plan.nqblk * plan.nsplit;
+  a.ragged = plan.ragged;
+  a.want_blocks = plan.want_blocks;
+  a.min_tiles = plan.min_tiles;
+  a.max_chunk_tiles = plan.max_chunk_tiles;
+  a.total_blocks = plan.ragged ? plan.max_items * Hkv * plan.nqblk
+                               : B * Hkv * plan.nqblk * plan.nsplit;
   a.anc_words = (N + 63) / 64;
   a.scale_log2 = scale * kLog2e;
   a.block_table = block_table;
@@ -834,10 +985,12 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
     while ((1 << a.page_shift) < page_size) ++a.page_shift;
     a.Lcap = max_blocks << a.page_shift;  // logical capacity of a sequence
   }
-  if (plan.nsplit > 1) {
-    const size_t rows = (size_t)B * Hkv * plan.nqblk * plan.rows * plan.nsplit;
+  if (plan.ragged || plan.nsplit > 1) {
+    const size_t rows = plan.ragged ? (size_t)plan.max_items * Hkv * plan.nqblk * plan.rows
+                                    : (size_t)B * Hkv * plan.nqblk * plan.rows * plan.nsplit;
     a.part_o = static_cast<float*>(ws);
     a.part_ml = static_cast<float*>(ws) + rows * D;
+    a.ragged_start = reinterpret_cast<int*>(a.part_ml + rows * 2);
   }
   hipError_t e;
   if (block_table != nullptr)
@@ -846,7 +999,7 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
   else
     e = (D == 128) ? launch_bf16<128, false>(a, plan.qbw, stream)
                    : launch_bf16<64, false>(a, plan.qbw, stream);
-  if (e != hipSuccess || plan.nsplit == 1) return e;
+  if (e != hipSuccess || (plan.nsplit == 1 && !plan.ragged)) return e;
   const size_t items = (size_t)B * Hkv * N * a.G * (D / 4);
   const dim3 grid((unsigned)((items + 255) / 256));
   if (D == 128)
