@@ -389,12 +389,181 @@ void gemm32w_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
   epilogue<MODE, MT>(acc, tl, s_key, keys, logits, part, M, V);
 }
 
+// LM head with argmax from 256 rows on: eight wavefronts (two per SIMD),
+// 256 W rows x 256 H rows per workgroup, both operands loaded straight from
+// memory into LDS in 64-wide k chunks, two stages.  With two wavefronts per
+// SIMD one wavefront's products run while the other waits at a barrier or on
+// its fragment reads; each wavefront owns 64 W rows x 128 H rows (128
+// accumulators per lane, so two fit a SIMD's registers).  Measured on the
+// 4096 x 2048 x 151936 product: 2374 us against 2682 us for gemm32w_kernel
+// (one wavefront per SIMD, W through registers).
+//   * W stage: half of a packed 128-wide chunk of two 128-row packed tiles,
+//     copied verbatim: slot ((tile * 8 + block) * 4 + piece) * 32 + lane' of
+//     16 bytes holds row lane' % 16 of that 16-row block at k = 8 piece +
+//     32 (lane' / 16) of the half chunk, so a fragment read of 16 rows is 256
+//     contiguous bytes;
+//   * H stage: 256 rows of 128 bytes; 16-byte piece x of row r sits at
+//     slot x ^ ((r / 2) % 8), which spreads the 16 rows of one fragment read
+//     over all the banks.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
+                         unsigned long long* __restrict__ keys, float* __restrict__ logits, int M,
+                         int K, int V, int nmt, int total_blocks) {
+  constexpr int KC = 64;           // k per stage
+  constexpr int TW = 256, TH = 256;
+  constexpr int NWAVE = 8;
+  constexpr int NT = NWAVE * 64;
+  constexpr int NWV = 4, NWH = 2;  // wavefronts along W and along H
+  constexpr int BW = TW / NWV / 32, BH = TH / NWH / 32;
+  constexpr int DMA = TW * KC * 2 / 1024 / NWAVE;  // 1 KB loads per wavefront per operand
+  __shared__ __attribute__((aligned(1024))) bf16_t sW0[TW * KC];
+  __shared__ __attribute__((aligned(1024))) bf16_t sW1[TW * KC];
+  __shared__ __attribute__((aligned(1024))) bf16_t sH0[TH * KC];
+  __shared__ __attribute__((aligned(1024))) bf16_t sH1[TH * KC];
+  __shared__ unsigned long long s_key[NWV][TH];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r32 = lane & 31, hh = lane >> 5;
+  const int wv = wave / NWH, wh = wave % NWH;
+  // which (H slice, W tile): groups of mg H slices per W tile on one die
+  const int nvt = total_blocks / nmt;
+  const int lid = xcd_remap(blockIdx.x, total_blocks);
+  const int mg = nmt % 4 == 0 ? 4 : (nmt % 2 == 0 ? 2 : 1);
+  const int r1 = lid / mg;
+  const int vt = r1 % nvt;
+  const int m0 = ((r1 / nvt) * mg + lid % mg) * TH;
+  const int nk128 = K / 128;
+  const int ntp = (V + kPT - 1) / kPT;  // packed 128-row tiles
+
+  // W: load q = wave * DMA + i copies 16-byte slots 64q .. 64q + 63, i.e.
+  // the halves of segments 2q and 2q + 1 (segment = (tile, block, piece))
+  size_t wbase[DMA];
+#pragma unroll
+  for (int i = 0; i < DMA; ++i) {
+    const int seg = 2 * (wave * DMA + i) + (lane >> 5);
+    const int ptl = seg >> 5, jj = (seg >> 2) & 7, sp = seg & 3;
+    int pt = 2 * vt + ptl;
+    pt = pt < ntp ? pt : ntp - 1;  // past the last tile: read it, drop the rows
+    wbase[i] = ((size_t)pt * nk128 * 32 + jj * 4 + sp) * 64 + (lane & 31);
+  }
+  // H: load i of wavefront w fills rows 8 (4w + i) .. + 7 (8 pieces each)
+  int hoff[DMA];
+#pragma unroll
+  for (int i = 0; i < DMA; ++i) {
+    const int row = (wave * DMA + i) * 8 + (lane >> 3);
+    const int x = (lane & 7) ^ ((row >> 1) & 7);
+    const int gr = m0 + row < M ? m0 + row : M - 1;
+    hoff[i] = gr * K + 8 * x;
+  }
+  auto dma = [&](bf16_t* sw, bf16_t* sh, int c) {
+    const size_t wc = ((size_t)(c >> 1) * 32 * 64 + (c & 1) * 32) * 8;
+#pragma unroll
+    for (int i = 0; i < DMA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(W + wbase[i] * 8 + wc),
+          (__attribute__((address_space(3))) void*)(sw + (wave * DMA + i) * 512), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < DMA; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(H + hoff[i] + (size_t)c * KC),
+          (__attribute__((address_space(3))) void*)(sh + (wave * DMA + i) * 512), 16, 0, 0);
+  };
+  auto wfrag = [&](const bf16_t* st, int r, int t) -> bf16x8_t {
+    const int x = 2 * t + hh;
+    const int slot = (((r >> 7) * 8 + ((r >> 4) & 7)) * 4 + (x & 3)) * 32 + (x >> 2) * 16 + (r & 15);
+    Frag8 f;
+    f.q = *reinterpret_cast<const u32x4_t*>(st + slot * 8);
+    return f.v;
+  };
+  auto hfrag = [&](const bf16_t* st, int r, int t) -> bf16x8_t {
+    const int pos = (2 * t + hh) ^ ((r >> 1) & 7);
+    Frag8 f;
+    f.q = *reinterpret_cast<const u32x4_t*>(st + r * KC + pos * 8);
+    return f.v;
+  };
+
+  f32x16_t acc[BW][BH];
+#pragma unroll
+  for (int i = 0; i < BW; ++i)
+#pragma unroll
+    for (int j = 0; j < BH; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = K / KC;
+  dma(sW0, sH0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __builtin_amdgcn_s_barrier();
+  // chunk c on stage U (compile-time: each stage one known LDS object); the
+  // loads of chunk c + 1 into the other stage go first, the chunk ends
+  // waiting for them
+  auto chunk = [&](int c, auto stage_tag) {
+    constexpr int U = decltype(stage_tag)::value;
+    const bf16_t* sw = U ? sW1 : sW0;
+    const bf16_t* sh = U ? sH1 : sH0;
+    dma(U ? sW0 : sW1, U ? sH0 : sH1, min(c + 1, nk - 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < KC / 16; ++t) {
+      bf16x8_t wf[BW], hf[BH];
+#pragma unroll
+      for (int i = 0; i < BW; ++i) wf[i] = wfrag(sw, wv * (TW / NWV) + 32 * i + r32, t);
+#pragma unroll
+      for (int j = 0; j < BH; ++j) hf[j] = hfrag(sh, wh * (TH / NWH) + 32 * j + r32, t);
+#pragma unroll
+      for (int i = 0; i < BW; ++i)
+#pragma unroll
+        for (int j = 0; j < BH; ++j) acc[i][j] = mfma32(wf[i], hf[j], acc[i][j]);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_barrier();
+  };
+  for (int c0 = 0; c0 < nk; c0 += 2) {
+    chunk(c0, std::integral_constant<int, 0>{});
+    chunk(c0 + 1, std::integral_constant<int, 1>{});
+  }
+
+  // acc[i][j][e]: W row v0 + 64 wv + 32 i + 8 (e / 4) + 4 hh + e % 4,
+  // H row m0 + 128 wh + 32 j + r32
+  const int vw0 = vt * TW + wv * (TW / NWV);
+#pragma unroll
+  for (int j = 0; j < BH; ++j) {
+    const int hrow = wh * (TH / NWH) + 32 * j + r32;
+    const int m = m0 + hrow;
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int i = 0; i < BW; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = vw0 + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (v < V) {
+          const unsigned long long key = argmax_key(acc[i][j][e], (uint32_t)v);
+          best = key > best ? key : best;
+          if (logits != nullptr && m < M) logits[(size_t)m * V + v] = acc[i][j][e];
+        }
+      }
+    const unsigned long long o = shfl_xor_u64(best, 32);
+    best = o > best ? o : best;
+    if (hh == 0) s_key[wv][hrow] = best;
+  }
+  __syncthreads();
+  for (int r = tid; r < TH; r += NT) {
+    if (m0 + r >= M) break;
+    unsigned long long k = s_key[0][r];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) k = s_key[w][r] > k ? s_key[w][r] : k;
+    keys[(size_t)(m0 + r) * nvt + vt] = k;
+  }
+}
+
 // The 256-row tile serves the LM head (one pass over k, argmax epilogue).
 // The split-K projections stay on 128-row tiles: with half as many tiles
 // they would take twice the splits, each with half the k range and twice
 // the partial sums, and measured slower (a 36-layer pass at 512 rows: 13.4
 // against 11.2 ms of projections).
 bool use_wide(int M) { return M >= kWideRows; }
+
+// The eight-wavefront LM head from this many rows on.
+constexpr int kGemm8Rows = 256;
+bool use_gemm8(int M) { return M >= kGemm8Rows; }
 
 }  // namespace
 
@@ -412,6 +581,14 @@ int gemm32_splits(int M, int K, int Nout) {
 hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
                                 unsigned long long* keys, float* logits, int M, int K, int V,
                                 hipStream_t stream) {
+  if (use_gemm8(M)) {
+    const int nmt = (M + 255) / 256;
+    const int total = nmt * gemm32_vtiles(V);
+    hipLaunchKernelGGL(gemm8_argmax_kernel, dim3(total), dim3(512), 0, stream,
+                       static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed),
+                       keys, logits, M, K, V, nmt, total);
+    return hipGetLastError();
+  }
   const int rows = use_wide(M) ? 256 : 128;
   const int nmt = (M + rows - 1) / rows;
   const int total = nmt * gemm32_vtiles(V);
