@@ -579,8 +579,10 @@ def tree_bench(args):
     calls (one per depth, each reading one row per frontier node) and the
     finish call.  A first, untimed pass drives the levels with the synthetic
     drafter and keeps each level's rows resident; the timed steps replay the
-    level calls on them, so the drafter itself is not timed.  The one-launch
-    builder on one row per depth is timed beside it."""
+    level calls on them, so the drafter itself is not timed; the timed build
+    is captured once as a HIP graph and replayed (device time of its
+    kernels), with the eagerly launched build and the one-launch builder on
+    one row per depth beside it."""
     import torch
 
     import tree_draft_verification_amd as tv
@@ -620,14 +622,34 @@ def tree_bench(args):
     for _ in range(args.warmup):
         build()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
+    # eager: every level call launched from the host (host-bound)
+    eager_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    eager_ev[0].record()
     for i in range(args.steps):
-        ev[i][0].record()
         build()
-        ev[i][1].record()
+    eager_ev[1].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    eager_us = eager_ev[0].elapsed_time(eager_ev[1]) * 1e3 / args.steps
+    # the value: the whole build captured once as a HIP graph and replayed,
+    # i.e. the device time of the level and finish kernels back to back
+    gs = torch.cuda.Stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    with torch.cuda.stream(gs):
+        build()
+        gs.synchronize()
+        tv.tv_graph_begin(gs)
+        build()
+        graph = tv.tv_graph_end(gs)
+        for _ in range(args.warmup):
+            graph.launch(gs)
+        gs.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(gs)
+            graph.launch(gs)
+            ev[i][1].record(gs)
+        gs.synchronize()
+        t1 = time.perf_counter()
     per = np.array([e[0].elapsed_time(e[1]) * 1e3 for e in ev])
     us = float(np.median(per))
     # rows read: one at level 1, W at every other level
@@ -667,6 +689,7 @@ def tree_bench(args):
                      "kernel": "whole build (top-k and level kernels per depth, finish kernel)",
                      "algorithmic_bytes": nbytes, "launch_us": round(us, 2)},
         "depth_rows_us": round(depth_rows_us, 2),
+        "eager_us": round(eager_us, 2),
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -62,10 +62,26 @@ __device__ void accept_sequence(AcceptLds& s, const int32_t* __restrict__ par,
                                 const int32_t* __restrict__ dr, const int32_t* __restrict__ tg,
                                 int N, int P) {
   const int tid = threadIdx.x;
-  // initial values: ptr = parent, ok = own match, dep = 1 (root: 0, 1, 0)
+  // initial values: ptr = parent, ok = own match, dep = 1 (root: 0, 1, 0).
+  // Every thread's parent and draft loads go out together, then every
+  // target load at those parents (clamped addresses, no branch around a
+  // load): two memory latencies per thread, not two per node.
+  constexpr int kPer = (TV_MAX_NODES + NT - 1) / NT;
+  int pv[kPer], dv[kPer], tv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = min(tid + u * NT, N - 1);
+    pv[u] = par[i];
+    dv[u] = dr[i];
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) tv[u] = tg[min(max(pv[u], 0), N - 1)];
   int bad = 0;
-  for (int i = tid; i < N; i += NT) {
-    const int p = par[i];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * NT;
+    if (i >= N) break;
+    const int p = pv[u];
     int ptr = 0, ok = 1, dep = 0;
     if (i == 0) {
       bad |= (p != -1);
@@ -73,7 +89,7 @@ __device__ void accept_sequence(AcceptLds& s, const int32_t* __restrict__ par,
       const bool valid = (p >= 0) && (p < i);
       bad |= !valid;
       ptr = valid ? p : 0;
-      ok = valid && (dr[i] == tg[ptr]);
+      ok = valid && (dv[u] == tv[u]);
       dep = 1;
     }
     s.par[i] = (int16_t)ptr;
@@ -87,7 +103,12 @@ __device__ void accept_sequence(AcceptLds& s, const int32_t* __restrict__ par,
   for (int round = 0; round < 11; ++round) {
     const int nxt = cur ^ 1;
     int active = 0;
-    for (int i = tid; i < N; i += NT) {
+    // the nodes of a thread are independent: unrolled, their LDS reads
+    // overlap instead of costing two round trips each
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * NT;
+      if (i >= N) break;
       const int q = s.ptr[cur][i];
       const int np = s.ptr[cur][q];
       s.ok[nxt][i] = s.ok[cur][i] & s.ok[cur][q];
@@ -101,8 +122,12 @@ __device__ void accept_sequence(AcceptLds& s, const int32_t* __restrict__ par,
 
   // deepest accepted node, smallest index on ties: maximise (dep, -index)
   int key = -1;
-  for (int i = tid; i < N; i += NT)
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * NT;
+    if (i >= N) break;
     if (s.ok[cur][i]) key = max(key, (int)s.dep[cur][i] * 65536 + (65535 - i));
+  }
   key = accept_wave_max(key);
   if constexpr (NT > 64) {
     if ((tid & 63) == 0) s.red[tid >> 6] = key;
