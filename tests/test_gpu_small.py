@@ -178,6 +178,9 @@ LM_CASES = {
     "M64_K256_V151936": Q8.replace(N=64, hidden=256, V=151936, seed=37),
     # ragged last tile (33 rows) after 781 whole ones
     "M17_K512_V100001": Q8.replace(B=1, N=17, hidden=512, V=100001, seed=38),
+    # the eight-wavefront product with its 384-row W tile (chosen: 2 rounds of
+    # 344 workgroups against 3 of 516), a partial last W tile and H slice
+    "M300_K256_V66000": Q8.replace(B=1, N=300, hidden=256, V=66000, seed=39),
 }
 
 

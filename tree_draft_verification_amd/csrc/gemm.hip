@@ -390,14 +390,12 @@ void gemm32w_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
 }
 
 // LM head with argmax from 256 rows on: eight wavefronts (two per SIMD),
-// 256 W rows x 256 H rows per workgroup, both operands loaded straight from
-// memory into LDS in 64-wide k chunks, two stages.  With two wavefronts per
-// SIMD one wavefront's products run while the other waits at a barrier or on
-// its fragment reads; each wavefront owns 64 W rows x 128 H rows (128
-// accumulators per lane, so two fit a SIMD's registers).  Measured on the
-// 4096 x 2048 x 151936 product: 2374 us against 2682 us for gemm32w_kernel
-// (one wavefront per SIMD, W through registers).
-//   * W stage: half of a packed 128-wide chunk of two 128-row packed tiles,
+// TW W rows (256 or 384) x 256 H rows per workgroup, both operands loaded
+// straight from memory into LDS in 64-wide k chunks, two stages.  With two
+// wavefronts per SIMD one wavefront's products run while the other waits at
+// a barrier or on its fragment reads; each wavefront owns TW/4 W rows x 128
+// H rows (TW/2 accumulators per lane, so two fit a SIMD's registers).
+//   * W stage: half of a packed 128-wide chunk of TW/128 packed tiles,
 //     copied verbatim: slot ((tile * 8 + block) * 4 + piece) * 32 + lane' of
 //     16 bytes holds row lane' % 16 of that 16-row block at k = 8 piece +
 //     32 (lane' / 16) of the half chunk, so a fragment read of 16 rows is 256
@@ -405,24 +403,32 @@ void gemm32w_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
 //   * H stage: 256 rows of 128 bytes; 16-byte piece x of row r sits at
 //     slot x ^ ((r / 2) % 8), which spreads the 16 rows of one fragment read
 //     over all the banks.
+// The 384-row tile takes all 160 KB of LDS (the epilogue's key table reuses
+// the first W stage) and 256 VGPRs; it reads 17 % fewer operand bytes per
+// product and 22 % fewer fragments per matrix instruction than the 256-row
+// tile, which measured 4-5 % faster on the 4096 x 2048 x 151936 product.
+template <int TW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
                          unsigned long long* __restrict__ keys, float* __restrict__ logits, int M,
                          int K, int V, int nmt, int total_blocks) {
   constexpr int KC = 64;           // k per stage
-  constexpr int TW = 256, TH = 256;
+  constexpr int TH = 256;
   constexpr int NWAVE = 8;
   constexpr int NT = NWAVE * 64;
   constexpr int NWV = 4, NWH = 2;  // wavefronts along W and along H
   constexpr int BW = TW / NWV / 32, BH = TH / NWH / 32;
-  constexpr int DMA = TW * KC * 2 / 1024 / NWAVE;  // 1 KB loads per wavefront per operand
+  constexpr int DMA_W = TW * KC * 2 / 1024 / NWAVE;  // 1 KB loads per wavefront
+  constexpr int DMA_H = TH * KC * 2 / 1024 / NWAVE;
   __shared__ __attribute__((aligned(1024))) bf16_t sW0[TW * KC];
   __shared__ __attribute__((aligned(1024))) bf16_t sW1[TW * KC];
   __shared__ __attribute__((aligned(1024))) bf16_t sH0[TH * KC];
   __shared__ __attribute__((aligned(1024))) bf16_t sH1[TH * KC];
-  __shared__ unsigned long long s_key[NWV][TH];
+  typedef unsigned long long KeyRow[TH];
+  static_assert(TW * KC * 2 >= NWV * TH * 8, "the key table fits a W stage");
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int r32 = lane & 31, hh = lane >> 5;
   const int wv = wave / NWH, wh = wave % NWH;
   // which (H slice, W tile): groups of mg H slices per W tile on one die
@@ -435,36 +441,33 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
   const int nk128 = K / 128;
   const int ntp = (V + kPT - 1) / kPT;  // packed 128-row tiles
 
-  // W: load q = wave * DMA + i copies 16-byte slots 64q .. 64q + 63, i.e.
-  // the halves of segments 2q and 2q + 1 (segment = (tile, block, piece))
-  size_t wbase[DMA];
-#pragma unroll
-  for (int i = 0; i < DMA; ++i) {
-    const int seg = 2 * (wave * DMA + i) + (lane >> 5);
-    const int ptl = seg >> 5, jj = (seg >> 2) & 7, sp = seg & 3;
-    int pt = 2 * vt + ptl;
-    pt = pt < ntp ? pt : ntp - 1;  // past the last tile: read it, drop the rows
-    wbase[i] = ((size_t)pt * nk128 * 32 + jj * 4 + sp) * 64 + (lane & 31);
-  }
-  // H: load i of wavefront w fills rows 8 (4w + i) .. + 7 (8 pieces each)
-  int hoff[DMA];
-#pragma unroll
-  for (int i = 0; i < DMA; ++i) {
-    const int row = (wave * DMA + i) * 8 + (lane >> 3);
-    const int x = (lane & 7) ^ ((row >> 1) & 7);
-    const int gr = m0 + row < M ? m0 + row : M - 1;
-    hoff[i] = gr * K + 8 * x;
-  }
+  // Addresses of the loads are formed per chunk (few VGPRs: the 384-row
+  // tile has none to spare).  W: load q = wave * DMA_W + i copies 16-byte
+  // slots 64q .. 64q + 63, the halves of segments 2q and 2q + 1 (segment =
+  // (tile, block, piece)); the packed tile of a load is the same for the
+  // whole wavefront, so its base is scalar.  Offsets in 16-byte units (below
+  // 2^31 for any supported V and K).  H: load i of wavefront w fills rows
+  // 8 (w * DMA_H + i) .. + 7, 8 pieces each.
+  const uint32_t wlane = (uint32_t)hh * 64 + r32;
   auto dma = [&](bf16_t* sw, bf16_t* sh, int c) {
-    const size_t wc = ((size_t)(c >> 1) * 32 * 64 + (c & 1) * 32) * 8;
+    const uint32_t wc = (uint32_t)(c >> 1) * 32 * 64 + (c & 1) * 32;
 #pragma unroll
-    for (int i = 0; i < DMA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(W + wbase[i] * 8 + wc),
-          (__attribute__((address_space(3))) void*)(sw + (wave * DMA + i) * 512), 16, 0, 0);
+    for (int i = 0; i < DMA_W; ++i) {
+      const int s0 = 2 * (wave * DMA_W + i);  // even: both halves in one packed tile
+      int pt = (TW / kPT) * vt + (s0 >> 5);
+      pt = pt < ntp ? pt : ntp - 1;           // past the last tile: read it, drop the rows
+      const uint32_t off = ((uint32_t)pt * nk128 * 32 + (s0 & 31)) * 64 + wc + wlane;
+      __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)off * 8),
+          (__attribute__((address_space(3))) void*)(sw + (wave * DMA_W + i) * 512), 16, 0, 0);
+    }
 #pragma unroll
-    for (int i = 0; i < DMA; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(H + hoff[i] + (size_t)c * KC),
-          (__attribute__((address_space(3))) void*)(sh + (wave * DMA + i) * 512), 16, 0, 0);
+    for (int i = 0; i < DMA_H; ++i) {
+      const int row = (wave * DMA_H + i) * 8 + (lane >> 3);
+      const int x = (lane & 7) ^ ((row >> 1) & 7);
+      const int gr = m0 + row < M ? m0 + row : M - 1;
+      __builtin_amdgcn_global_load_lds((const void*)(H + (size_t)gr * K + 8 * x + (size_t)c * KC),
+          (__attribute__((address_space(3))) void*)(sh + (wave * DMA_H + i) * 512), 16, 0, 0);
+    }
   };
   auto wfrag = [&](const bf16_t* st, int r, int t) -> bf16x8_t {
     const int x = 2 * t + hh;
@@ -521,8 +524,10 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
     chunk(c0 + 1, std::integral_constant<int, 1>{});
   }
 
-  // acc[i][j][e]: W row v0 + 64 wv + 32 i + 8 (e / 4) + 4 hh + e % 4,
-  // H row m0 + 128 wh + 32 j + r32
+  // acc[i][j][e]: W row v0 + TW/4 wv + 32 i + 8 (e / 4) + 4 hh + e % 4,
+  // H row m0 + 128 wh + 32 j + r32.  Every read of the stages is done (the
+  // loop ends at a barrier), so the key table can take the first W stage.
+  KeyRow* s_key = reinterpret_cast<KeyRow*>(sW0);
   const int vw0 = vt * TW + wv * (TW / NWV);
 #pragma unroll
   for (int j = 0; j < BH; ++j) {
@@ -561,13 +566,31 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
 // against 11.2 ms of projections).
 bool use_wide(int M) { return M >= kWideRows; }
 
-// The eight-wavefront LM head from this many rows on.
+// The eight-wavefront LM head from this many rows on, and its W tile.  One
+// workgroup fits a CU, so the grid runs in rounds of 256 workgroups: the
+// 384-row tile (about 5 % cheaper per product, 1.5x the work per
+// workgroup) is taken when its rounds cost less.  Measured: 256 rows
+// (594 -> 396 workgroups, 3 -> 2 rounds) 393 -> 380 us; 512 rows (1188 ->
+// 792, 5 -> 4 rounds of 1.5x work) 636 -> 687 us, so 256 there; 4096 rows
+// 2238-2326 -> 2225 us.
 constexpr int kGemm8Rows = 256;
+constexpr int kCUs = 256;
 bool use_gemm8(int M) { return M >= kGemm8Rows; }
+int gemm8_tile(int M, int V) {
+  const long nmt = (M + 255) / 256;
+  const long r256 = (nmt * ((V + 255) / 256) + kCUs - 1) / kCUs;
+  const long r384 = (nmt * ((V + 383) / 384) + kCUs - 1) / kCUs;
+  return r384 * 1.5 * 0.95 < (double)r256 ? 384 : 256;
+}
 
 }  // namespace
 
 int gemm32_vtiles(int V) { return (V + kWT - 1) / kWT; }
+
+int gemm_argmax_vtiles(int M, int V) {
+  const int tw = use_gemm8(M) ? gemm8_tile(M, V) : kWT;
+  return (V + tw - 1) / tw;
+}
 
 int gemm32_splits(int M, int K, int Nout) {
   const int tiles = ((M + 127) / 128) * gemm32_vtiles(Nout);
@@ -583,10 +606,15 @@ hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
                                 hipStream_t stream) {
   if (use_gemm8(M)) {
     const int nmt = (M + 255) / 256;
-    const int total = nmt * gemm32_vtiles(V);
-    hipLaunchKernelGGL(gemm8_argmax_kernel, dim3(total), dim3(512), 0, stream,
-                       static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed),
-                       keys, logits, M, K, V, nmt, total);
+    const int total = nmt * gemm_argmax_vtiles(M, V);
+    if (gemm8_tile(M, V) == 384)
+      hipLaunchKernelGGL(gemm8_argmax_kernel<384>, dim3(total), dim3(512), 0, stream,
+                         static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed),
+                         keys, logits, M, K, V, nmt, total);
+    else
+      hipLaunchKernelGGL(gemm8_argmax_kernel<256>, dim3(total), dim3(512), 0, stream,
+                         static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed),
+                         keys, logits, M, K, V, nmt, total);
     return hipGetLastError();
   }
   const int rows = use_wide(M) ? 256 : 128;

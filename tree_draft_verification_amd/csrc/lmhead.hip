@@ -746,7 +746,7 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
   const bool pk = w_layout == TV_LAYOUT_PACKED;
   const dim3 grid(total), block(kThreads);
   if (mb != 4) {
-    const size_t pbytes = (size_t)M * (pk ? gemm32_vtiles(V) : nvt) * 8;
+    const size_t pbytes = (size_t)M * (pk ? gemm_argmax_vtiles(M, V) : nvt) * 8;
     keys = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) +
                                                  ((ws_bytes - pbytes) & ~(size_t)255));
   }
@@ -755,7 +755,7 @@ hipError_t launch_lmhead_argmax(const void* hidden, const void* w, int32_t* argm
     hipError_t e = launch_gemm32_argmax(h, wv, keys, logits, M, K, V, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(argmax_reduce_kernel, dim3((M + 3) / 4), dim3(256), 0, stream, keys,
-                       argmax, M, gemm32_vtiles(V));
+                       argmax, M, gemm_argmax_vtiles(M, V));
     return hipGetLastError();
   }
 #define TV_LM_LAUNCH(P, MBV, MODEV)                                                         \

@@ -145,6 +145,7 @@ hipError_t launch_accept_compact(const int32_t* parent, const int32_t* draft,
 // ---------------------------------------------------------------- products with M > 64 rows
 
 int gemm32_vtiles(int V);                  // 256-row W tiles
+int gemm_argmax_vtiles(int M, int V);      // W tiles (keys per row) of the M > 64 argmax product
 int gemm32_splits(int M, int K, int Nout);
 hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
                                 unsigned long long* keys, float* logits, int M, int K, int V,
