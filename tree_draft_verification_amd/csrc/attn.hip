@@ -90,15 +90,22 @@ __device__ __forceinline__ void flag(int32_t* st, int b, int f) {
   if (st) atomicOr(&st[b], f);
 }
 
+// max(x, y) of scores that are never NaN, as the median of (x, y, +inf):
+// one v_max3 covers two of them, with none of the quieting that fmaxf's
+// NaN rules add in front of every v_max.
+__device__ __forceinline__ float smax(float x, float y) {
+  return __builtin_amdgcn_fmed3f(x, y, __builtin_inff());
+}
+
 // Reductions across the four 16-lane groups of a wavefront (lanes l, l^16,
 // l^32, l^48) with the gfx950 row/half swaps: each swap returns both
 // operands exchanged, so combining its two results pairs every lane with
 // its partner without a trip through LDS.
 __device__ __forceinline__ float max_across_groups(float x) {
   auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  x = smax(__uint_as_float(h[0]), __uint_as_float(h[1]));
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return smax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_across_groups(float x) {
   auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -444,9 +451,17 @@ void attn_bf16_kernel(AttnArgs a) {
 
   // One tile's products once its K rows and V are in LDS (read through
   // kfrag and vfrag): S^T = K Q^T, mask, online softmax, O^T += V^T P^T.
+  // All K fragments of the tile are read before the first product and all
+  // V fragments before the softmax, so each phase waits on LDS once instead
+  // of once per fragment.
   auto compute_tile = [&](int nvalid, int tt, auto kfrag, auto vfrag) {
     const bool tree = tt >= 0;
     const bool need_mask = tree || nvalid < kKT;
+    Frag8 kf[4][DS];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < DS; ++ks) kf[kb][ks].u = kfrag(kb, ks);
     // S^T = K Q^T: lane holds query column l16, keys kb*16 + 4*kg + r.
     f32x4_t s[QBW][4];
 #pragma unroll
@@ -454,39 +469,50 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < DS; ++ks) {
-        Frag8 kf;
-        kf.u = kfrag(kb, ks);
+      for (int ks = 0; ks < DS; ++ks)
 #pragma unroll
-        for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = mfma16x16x32(kf.v, qf[qb][ks], s[qb][kb]);
-      }
+        for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = mfma16x16x32(kf[kb][ks].v, qf[qb][ks], s[qb][kb]);
     }
+    // O^T += V^T P^T below reads these (the first half of the output rows'
+    // fragments are in flight during the softmax, the second half during the
+    // first half's products); k-slot e of lane group kg is key 32u + 4kg + e
+    // (e < 4) or 32u + 16 + 4kg + e - 4 (e >= 4), in both operands.
+    constexpr int DH = DB / 2;
+    Frag8 vf[DB][2];
+#pragma unroll
+    for (int db = 0; db < DH; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) vf[db][u].u = vfrag(db, u);
 
     // mask (only where needed), then the online softmax in the exp2 domain
     Frag8 pf[QBW][2];
 #pragma unroll
     for (int qb = 0; qb < QBW; ++qb) {
       if (need_mask) {
-        const unsigned long long word =
-            tree ? sAnc[(qnode[qb] - node_lo) * W + tt] : ~0ull;
+        // visible keys of this query as a 64-bit word (ancestor bits, keys
+        // past the tile's valid rows cleared); this lane's keys kb*16 +
+        // 4kg + r are bits kb*16 + r of the word shifted right by 4kg
+        unsigned long long word = tree ? sAnc[(qnode[qb] - node_lo) * W + tt] : ~0ull;
+        if (nvalid < kKT) word &= (1ull << nvalid) - 1ull;
+        const uint32_t wlo = (uint32_t)(word >> (4 * kg));
+        const uint32_t whi = (uint32_t)(word >> (32 + 4 * kg));
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int key = kb * 16 + 4 * kg + r;
-            const bool vis = key < nvalid && ((word >> key) & 1ull);
-            s[qb][kb][r] = vis ? s[qb][kb][r] : -INFINITY;
+            const uint32_t bit = ((kb < 2 ? wlo : whi) >> ((kb & 1) * 16 + r)) & 1u;
+            s[qb][kb][r] = bit ? s[qb][kb][r] : -INFINITY;
           }
       }
-      float tmax = -INFINITY;
+      float mk[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        tmax = fmaxf(fmaxf(fmaxf(tmax, s[qb][kb][0]), fmaxf(s[qb][kb][1], s[qb][kb][2])),
-                     s[qb][kb][3]);
+        mk[kb] = smax(smax(s[qb][kb][0], s[qb][kb][1]), smax(s[qb][kb][2], s[qb][kb][3]));
+      float tmax = smax(smax(mk[0], mk[1]), smax(mk[2], mk[3]));
       tmax = max_across_groups(tmax);
       const float tm = tmax * a.scale_log2;  // scale > 0, so max commutes
       if (__any(tm > m_ref[qb] + kLazy)) {
-        const float m_new = fmaxf(m_ref[qb], tm);
+        const float m_new = smax(m_ref[qb], tm);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         l_run[qb] *= alpha;
 #pragma unroll
@@ -494,16 +520,15 @@ void attn_bf16_kernel(AttnArgs a) {
         m_ref[qb] = m_new;
       }
       const float mu = (m_ref[qb] == -INFINITY) ? 0.f : m_ref[qb];
-      float psum = 0.f;
       float p[4][4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], a.scale_log2, -mu));
-          psum += p[kb][r];
-        }
-      l_run[qb] += psum;
+        for (int r = 0; r < 4; ++r) p[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][r], a.scale_log2, -mu));
+      float ps[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) ps[kb] = (p[kb][0] + p[kb][1]) + (p[kb][2] + p[kb][3]);
+      l_run[qb] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         pf[qb][u].u = make_uint4(pack_bf16x2(p[2 * u][0], p[2 * u][1]),
@@ -512,18 +537,16 @@ void attn_bf16_kernel(AttnArgs a) {
                                  pack_bf16x2(p[2 * u + 1][2], p[2 * u + 1][3]));
     }
 
-    // O^T += V^T P^T; k-slot e of lane group kg is key 32u + 4kg + e (e < 4)
-    // or 32u + 16 + 4kg + e - 4 (e >= 4), in both operands.
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = DH; db < DB; ++db)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        Frag8 vf;
-        vf.u = vfrag(db, u);
+      for (int u = 0; u < 2; ++u) vf[db][u].u = vfrag(db, u);
 #pragma unroll
-        for (int qb = 0; qb < QBW; ++qb) o[qb][db] = mfma16x16x32(vf.v, pf[qb][u].v, o[qb][db]);
-      }
-    }
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int qb = 0; qb < QBW; ++qb) o[qb][db] = mfma16x16x32(vf[db][u].v, pf[qb][u].v, o[qb][db]);
   };
 
   if constexpr (kDma) {
