@@ -23,6 +23,7 @@ from .verify import (  # noqa: F401
     kv_compact_paged,
     lm_head_argmax,
     paged_to_contiguous,
+    round_bf16,
     lm_logits,
     tree_accept,
     tree_attention,

@@ -35,7 +35,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .verify import ancestors, decode, kv_compact, tree_attention
+from .verify import ancestors, decode, kv_compact, round_bf16, tree_attention
 
 
 def rms_norm(x, w, eps: float) -> np.ndarray:
@@ -74,7 +74,7 @@ def node_positions(parent, seq_lens) -> np.ndarray:
 
 
 def verify_pass(dims: dict, weights: dict, tokens, parent, seq_lens, k_cache, v_cache,
-                logit_rows=None, v_chunk: int = 8192) -> dict:
+                logit_rows=None, v_chunk: int = 8192, bf16_points: bool = False) -> dict:
     """The multi-layer pass over one draft tree per sequence.
 
     dims: layers, hidden, Hq, Hkv, D, inter, V, eps, theta.
@@ -85,6 +85,15 @@ def verify_pass(dims: dict, weights: dict, tokens, parent, seq_lens, k_cache, v_
     Returns the final normalised hidden states [B*N][hidden], the argmax and
     top-2 gap of every row, the logits of ``logit_rows`` (all rows if None),
     and fp64 copies of the caches with the tree rows written.
+
+    bf16_points=True is not the definition but a model of a pipeline that
+    stores its activations in bf16: every normalised input of a product (h
+    after each norm), q, the k and v rows written to the caches, the
+    attention output, the MLP activation silu(g) * u, the probabilities that
+    multiply V, and the LM head's input are rounded to bf16 where they are
+    produced; the residual stream, all sums and the returned (fp32-stored)
+    final hidden states stay exact.  The distance between the two modes
+    sizes the tolerance of a bf16 implementation.
     """
     Ly, Hd = dims["layers"], dims["hidden"]
     Hq, Hkv, D, I = dims["Hq"], dims["Hkv"], dims["D"], dims["inter"]
@@ -99,24 +108,28 @@ def verify_pass(dims: dict, weights: dict, tokens, parent, seq_lens, k_cache, v_
     emb = np.asarray(weights["embed"])
     x = decode(emb[tokens.reshape(-1)], "bf16")                 # [M][hidden]
     scale = 1.0 / np.sqrt(D)
+    rnd = round_bf16 if bf16_points else (lambda t: t)
     for ly in range(Ly):
-        h = rms_norm(x, decode(weights["ln1"][ly], "bf16"), eps)
+        h = rnd(rms_norm(x, decode(weights["ln1"][ly], "bf16"), eps))
         qkv = h @ decode(weights["w_qkv"][ly], "bf16").T         # [M][(Hq+2Hkv)D]
         q = qkv[:, :Hq * D].reshape(B, N, Hq, D)
         k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(B, N, Hkv, D)
         v = qkv[:, (Hq + Hkv) * D:].reshape(B, N, Hkv, D)
-        q = rope(rms_norm(q, decode(weights["q_norm"][ly], "bf16"), eps), pos[:, :, None], theta)
-        k = rope(rms_norm(k, decode(weights["k_norm"][ly], "bf16"), eps), pos[:, :, None], theta)
+        q = rnd(rope(rms_norm(q, decode(weights["q_norm"][ly], "bf16"), eps), pos[:, :, None], theta))
+        k = rnd(rope(rms_norm(k, decode(weights["k_norm"][ly], "bf16"), eps), pos[:, :, None], theta))
+        v = rnd(v)
         for b in range(B):
             L = int(seq_lens[b])
             Kc[ly, b, :, L:L + N] = k[b].transpose(1, 0, 2)
             Vc[ly, b, :, L:L + N] = v[b].transpose(1, 0, 2)
-        o = tree_attention(q, Kc[ly], Vc[ly], seq_lens, parent, scale, "f64")
+        o = rnd(tree_attention(q, Kc[ly], Vc[ly], seq_lens, parent, scale, "f64",
+                               p_round=round_bf16 if bf16_points else None))
         x = x + o.reshape(M, Hq * D) @ decode(weights["w_o"][ly], "bf16").T
-        h = rms_norm(x, decode(weights["ln2"][ly], "bf16"), eps)
+        h = rnd(rms_norm(x, decode(weights["ln2"][ly], "bf16"), eps))
         gu = h @ decode(weights["w_gu"][ly], "bf16").T           # [M][2I]
-        x = x + (silu(gu[:, :I]) * gu[:, I:]) @ decode(weights["w_down"][ly], "bf16").T
+        x = x + rnd(silu(gu[:, :I]) * gu[:, I:]) @ decode(weights["w_down"][ly], "bf16").T
     hf = rms_norm(x, decode(weights["final_norm"], "bf16"), eps)
+    hl = rnd(hf)                                                # the LM head's input
     V = dims["V"]
     lm = np.asarray(weights["lm_head"])
     top1 = np.full(M, -np.inf)
@@ -125,7 +138,7 @@ def verify_pass(dims: dict, weights: dict, tokens, parent, seq_lens, k_cache, v_
     rows = np.arange(M) if logit_rows is None else np.asarray(logit_rows, dtype=np.int64)
     logits = np.empty((len(rows), V))
     for v0 in range(0, V, v_chunk):
-        lg = hf @ decode(lm[v0:v0 + v_chunk], "bf16").T          # [M][chunk]
+        lg = hl @ decode(lm[v0:v0 + v_chunk], "bf16").T          # [M][chunk]
         logits[:, v0:v0 + lg.shape[1]] = lg[rows]
         # merge this chunk's two largest values into the running top-2
         part = np.sort(np.partition(lg, -2, axis=1)[:, -2:] if lg.shape[1] > 1

@@ -34,6 +34,20 @@ def decode(x, dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
+def round_bf16(x) -> np.ndarray:
+    """The fp64 value of x stored as bf16: binary32's sign, exponent and top 7
+    fraction bits, rounded to nearest with ties to even (x is first rounded
+    to binary32).  Not used by the functions below unless a caller asks for a
+    model of bf16 storage (``p_round`` and the pass's ``bf16_points``), which
+    only sizes tolerances."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    finite = np.isfinite(f)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    r = np.where(finite, r, u & 0xFFFF0000)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 # ----------------------------------------------------------------------------
 # tree topology
 
@@ -60,7 +74,7 @@ def ancestors(parent_row, i: int) -> list[int]:
 # step 1: tree-causal attention
 
 def tree_attention(q, k_cache, v_cache, seq_lens, parent, scale, dtype,
-                   node_chunk: int = 128, nodes=None) -> np.ndarray:
+                   node_chunk: int = 128, nodes=None, p_round=None) -> np.ndarray:
     """Output of every (sequence b, node i, query head h), in fp64.
 
     Definition (JetSpec GitHub README, "JetSpec > Overview": the whole tree
@@ -72,7 +86,10 @@ def tree_attention(q, k_cache, v_cache, seq_lens, parent, scale, dtype,
     Query head h reads KV head h // G.  The prefix scores of a chunk of nodes
     are one matmul; the softmax is taken over the union of both key sets.
     ``nodes`` restricts the work to those node indices (in every sequence);
-    the other outputs are left as NaN.
+    the other outputs are left as NaN.  ``p_round``, if given, is applied to
+    the unnormalised probabilities that multiply V (not to their sum): a
+    model of a kernel that feeds them to the second product in a narrower
+    type, used only to size tolerances.
     """
     Q = decode(q, dtype)
     K = decode(k_cache, dtype)
@@ -104,6 +121,8 @@ def tree_attention(q, k_cache, v_cache, seq_lens, parent, scale, dtype,
                     p_pre = np.exp(sp - m)
                     p_anc = np.exp(s_anc - m)
                     den = p_pre.sum(axis=1) + p_anc.sum(axis=1)
+                    if p_round is not None:
+                        p_pre, p_anc = p_round(p_pre), p_round(p_anc)
                     o = p_pre @ Vp + p_anc @ Va
                     out[b, i, g * G:(g + 1) * G] = o / den[:, None]
     return out

@@ -1,42 +1,63 @@
 """GPU parity of the multi-layer verification pass against the fp64 oracle
 (oracle.model), of the one-launch multi-layer compaction, and of graph
 replay of the whole step against its eager run."""
+import json
+import os
+
 import numpy as np
 import pytest
 
 import oracle
-from workloads import MODELS, WORKLOADS, model_inputs, model_weights
+from workloads import MODEL_CASES, MODELS, WORKLOADS, model_inputs, model_weights
 
 from _helpers import i32_dev, to_dev, to_host_bits, to_host_f64
 
 pytestmark = pytest.mark.gpu
 
 # Tolerances of the pass (bf16 activations between kernels, fp32 accumulation)
-# against the fp64 oracle.  They come from the oracle's own spread when every
-# activation the GPU rounds is perturbed by +-2^-9 (relative): 3.4e-3 at 3
-# layers and 1.18e-2 at 36 layers of the Qwen3-8B shape.
-SMALL_REL_L2 = 5e-3        # hidden, cache rows and logits of the 2-3 layer stacks
-SMALL_ARGMAX_GAP_EXEMPT = 1e-2
-FULL_HIDDEN_REL_L2 = 3e-2  # 36 layers
-FULL_CACHE_REL_L2 = 1e-2
-FULL_ARGMAX_GAP_EXEMPT = 5e-2
+# against the fp64 oracle.  tests/golden/model_tolerance.json holds, per case,
+# how far the oracle itself moves when every activation the pass stores is
+# rounded to bf16 (oracle.verify_pass(..., bf16_points=True), written by
+# tests/golden/make_model_tolerance.py).  The GPU pass carries rounding noise
+# of that size in another realisation, plus fp32 accumulation terms orders of
+# magnitude smaller: its rel-L2 distances may be up to REL_MARGIN times the
+# model's.  A greedy token may differ from the oracle's only if the token the
+# GPU picked has an exact logit within twice the largest logit change the GPU
+# may make (REL_MARGIN times the model's) of the exact maximum: a flip needs
+# the two logits to move apart by their gap.
+REL_MARGIN = 2.0
+with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                       "model_tolerance.json")) as _f:
+    TOL = json.load(_f)
 
-Q8 = WORKLOADS["qwen3_8b_L1024_N64"]
-CASES = {
-    "tiny_d64_B2_ragged": ("tiny_d64", WORKLOADS["qwen3_8b_ragged8_N64"].replace(
-        B=2, Hq=4, Hkv=2, D=64, N=12, L_lo=20, L_hi=70, seed=5)),
-    "small_d128_L300_N64": ("small_d128", Q8.replace(Hq=8, Hkv=2, L_lo=300, L_hi=300, seed=61)),
-    "small_d128_B3_N40_M120": ("small_d128", WORKLOADS["qwen3_8b_ragged8_N64"].replace(
-        B=3, Hq=8, Hkv=2, N=40, L_lo=10, L_hi=200, seed=62)),
-    # unsplit gate/up projection with the fused silu(gate) * up epilogue
-    "wide_mlp_N64_L200": ("wide_mlp", Q8.replace(Hq=2, Hkv=1, L_lo=200, L_hi=200, seed=63)),
-    # 512 and 640 rows: the products with 256-row H tiles (the last slice of
-    # 640 rows half empty)
-    "small_d128_B8_N64_M512": ("small_d128", WORKLOADS["qwen3_8b_ragged8_N64"].replace(
-        B=8, Hq=8, Hkv=2, N=64, L_lo=10, L_hi=120, seed=64)),
-    "small_d128_B10_N64_M640": ("small_d128", WORKLOADS["qwen3_8b_ragged8_N64"].replace(
-        B=10, Hq=8, Hkv=2, N=64, L_lo=10, L_hi=90, seed=65)),
-}
+
+def _bounds(name):
+    t = TOL[name]
+    return dict(hidden=REL_MARGIN * t["hidden_rel_l2"], cache=REL_MARGIN * t["cache_rel_l2"],
+                logits=REL_MARGIN * t["logits_rel_l2"],
+                gap=2 * REL_MARGIN * t["logit_max_abs_change"])
+
+
+CASES = {k: v for k, v in MODEL_CASES.items() if v[0] != "qwen3_8b"}
+
+
+def _bad_argmax(got, ref, bound):
+    """Rows whose GPU token differs from the oracle's and whose exact logit is
+    further than ``bound`` below the exact maximum (ref holds every row's
+    logits)."""
+    rows = np.arange(len(got))
+    picked = ref["logits"][rows, got]
+    return (got != ref["argmax"]) & (picked < ref["top1"] - bound)
+
+
+def _tree_rows(cache, seq_lens, N):
+    return np.concatenate([cache[:, b, :, int(L):int(L) + N].ravel()
+                           for b, L in enumerate(seq_lens)])
+
+
+def _cache_rel(gk, gv, ref, x, N):
+    return max(_rel(_tree_rows(gk, x["seq_lens"], N), _tree_rows(ref["k_cache"], x["seq_lens"], N)),
+               _rel(_tree_rows(gv, x["seq_lens"], N), _tree_rows(ref["v_cache"], x["seq_lens"], N)))
 
 
 def _dims_torch(cfg):
@@ -82,15 +103,17 @@ def test_pass_matches_oracle(name):
     arg, lg, hid, k, v = _run_pass(model, x, wl)
     ref = oracle.verify_pass(cfg.dims(), w, x["tokens"], x["parent"], x["seq_lens"],
                              x["k_cache"], x["v_cache"])
+    bd = _bounds(name)
     rl = _rel(lg.cpu().numpy().astype(np.float64), ref["logits"])
     rh = _rel(hid.cpu().numpy().astype(np.float64), ref["hidden"])
     gk, gv = to_host_f64(k), to_host_f64(v)
-    rc = max(_rel(gk, ref["k_cache"]), _rel(gv, ref["v_cache"]))
+    rc = _cache_rel(gk, gv, ref, x, wl.N)
     got = arg.cpu().numpy()
-    bad = (got != ref["argmax"]) & (ref["gap"] >= SMALL_ARGMAX_GAP_EXEMPT)
+    bad = _bad_argmax(got, ref, bd["gap"])
     print(f"[pass] {name}: logits rel={rl:.2e} hidden rel={rh:.2e} cache rel={rc:.2e} "
-          f"argmax diffs={(got != ref['argmax']).sum()} (non-exempt {bad.sum()})", flush=True)
-    assert rl <= SMALL_REL_L2 and rh <= SMALL_REL_L2 and rc <= SMALL_REL_L2
+          f"argmax diffs={(got != ref['argmax']).sum()} (non-exempt {bad.sum()}); bounds {bd}",
+          flush=True)
+    assert rl <= bd["logits"] and rh <= bd["hidden"] and rc <= bd["cache"]
     assert not bad.any(), f"argmax differs at rows {np.nonzero(bad)[0]}"
     # rows the pass must not touch: prefix bits and the NaN rows past the tree
     kb = to_host_bits(k)
@@ -230,8 +253,9 @@ def test_pass_full_size_qwen3_8b(wname):
     """All 36 Qwen3-8B-shaped layers over the full workload, every row, in
     the launch configuration the benchmark times."""
     import time
-    cfg = MODELS["qwen3_8b"]
-    wl = WORKLOADS[wname]
+    mname, wl = MODEL_CASES[wname]
+    cfg = MODELS[mname]
+    bd = _bounds(wname)
     t0 = time.time()
     w = model_weights(cfg)
     x = model_inputs(cfg, wl)
@@ -242,15 +266,15 @@ def test_pass_full_size_qwen3_8b(wname):
     del model, k, v
     print(f"[pass-full] {wname}: GPU pass done at {time.time() - t0:.0f} s", flush=True)
     ref = oracle.verify_pass(cfg.dims(), w, x["tokens"], x["parent"], x["seq_lens"],
-                             x["k_cache"], x["v_cache"], logit_rows=[0])
+                             x["k_cache"], x["v_cache"])
     print(f"[pass-full] {wname}: oracle done at {time.time() - t0:.0f} s", flush=True)
     rh = _rel(got_h.astype(np.float64), ref["hidden"])
-    rc = max(_rel(gk, ref["k_cache"]), _rel(gv, ref["v_cache"]))
-    bad = (got != ref["argmax"]) & (ref["gap"] >= FULL_ARGMAX_GAP_EXEMPT)
+    rc = _cache_rel(gk, gv, ref, x, wl.N)
+    bad = _bad_argmax(got, ref, bd["gap"])
     print(f"[pass-full] {wname}: hidden rel={rh:.2e} cache rel={rc:.2e} argmax diffs="
           f"{(got != ref['argmax']).sum()} (non-exempt {bad.sum()}), min gap "
-          f"{ref['gap'].min():.3e}", flush=True)
-    assert rh <= FULL_HIDDEN_REL_L2 and rc <= FULL_CACHE_REL_L2
+          f"{ref['gap'].min():.3e}; bounds {bd}", flush=True)
+    assert rh <= bd["hidden"] and rc <= bd["cache"]
     assert not bad.any()
 
 
@@ -263,18 +287,18 @@ def test_pass_workspace_needs_no_initial_contents():
     for name in ("small_d128_L300_N64", "small_d128_B3_N40_M120", "small_d128_L300_N64"):
         mname, wl = CASES[name]
         cfg = MODELS[mname]
-        runs.append((cfg, wl, model_weights(cfg), model_inputs(cfg, wl)))
-    model = _model_dev(runs[0][0], runs[0][2])
+        runs.append((name, cfg, wl, model_weights(cfg), model_inputs(cfg, wl)))
+    model = _model_dev(runs[0][1], runs[0][3])
     need = max(tv.tv_verify_pass_workspace(model, wl.B, wl.N, int(x["seq_lens"].max()))
-               for _, wl, _, x in runs)
+               for _, _, wl, _, x in runs)
     ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
-    for cfg, wl, w, x in runs:
+    for name, cfg, wl, w, x in runs:
         k, v = to_dev(x["k_cache"], "bf16"), to_dev(x["v_cache"], "bf16")
         arg = tv.tv_verify_pass(model, i32_dev(x["tokens"]), i32_dev(x["parent"]),
                                 i32_dev(x["seq_lens"]), k, v,
                                 max_seq_len=int(x["seq_lens"].max()), workspace=ws)
         ref = oracle.verify_pass(cfg.dims(), w, x["tokens"], x["parent"], x["seq_lens"],
-                                 x["k_cache"], x["v_cache"], logit_rows=[])
+                                 x["k_cache"], x["v_cache"])
         got = arg.cpu().numpy()
-        bad = (got != ref["argmax"]) & (ref["gap"] >= SMALL_ARGMAX_GAP_EXEMPT)
+        bad = _bad_argmax(got, ref, _bounds(name)["gap"])
         assert not bad.any(), f"{wl.B}x{wl.N}: argmax differs at rows {np.nonzero(bad)[0]}"

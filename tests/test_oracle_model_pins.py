@@ -246,3 +246,62 @@ def test_m8_greedy_decoding_is_consistent_with_one_chain_pass():
         L = int(x["seq_lens"][b])
         np.testing.assert_allclose(ar["k_cache"][:, b, :, L:L + n], r["k_cache"][:, b, :, L:L + n],
                                    rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------- bf16 storage model
+
+
+def test_m9_round_bf16_hand_values_and_invariants():
+    """Round to nearest, ties to even, at 7 fraction bits (spacing 2^-7 at 1)."""
+    r = oracle.round_bf16
+    e = 2.0 ** -8
+    cases = [(1.0, 1.0), (1 + e, 1.0),                    # tie -> even (1.0)
+             (1 + 3 * e, 1 + 4 * e),                       # tie -> even (1 + 2^-6)
+             (1 + e + 2.0 ** -20, 1 + 2 * e),              # above the tie
+             (-(1 + 3 * e), -(1 + 4 * e)), (65535.0, 65536.0),
+             (3.14159265358979, 3.140625), (0.1, 0.10009765625), (0.0, 0.0)]
+    for x, want in cases:
+        assert r(np.array([x]))[0] == want, x
+    assert np.isinf(r(np.array([np.inf]))[0]) and np.isnan(r(np.array([np.nan]))[0])
+    # every finite bf16 value is its own rounding; relative error <= 2^-8
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        vals = oracle.decode(bits, "bf16")
+    fin = np.isfinite(vals)
+    np.testing.assert_array_equal(r(vals[fin]), vals[fin])
+    x = np.random.default_rng(3).standard_normal(100_000) * 10.0 ** np.random.default_rng(4).uniform(-20, 20, 100_000)
+    y = r(x)
+    np.testing.assert_array_equal(r(y), y)
+    assert np.all(np.abs(y - x) <= 2.0 ** -8 * np.abs(x))
+
+
+def test_m10_bf16_storage_model_rounds_what_it_names_and_only_perturbs():
+    """With bf16_points the written cache rows are bf16 values; the pass moves by about the rounding size (2^-9 relative per
+    stored value), not by more, and the prefix rows stay as they were."""
+    w = model_weights(CFG)
+    x = model_inputs(CFG, WL)
+    args = (CFG.dims(), w, x["tokens"], x["parent"], x["seq_lens"], x["k_cache"], x["v_cache"])
+    ex = oracle.verify_pass(*args)
+    rd = oracle.verify_pass(*args, bf16_points=True)
+    for b, L in enumerate(x["seq_lens"]):
+        L = int(L)
+        for c in ("k_cache", "v_cache"):
+            t = rd[c][:, b, :, L:L + WL.N]
+            np.testing.assert_array_equal(oracle.round_bf16(t), t)
+            np.testing.assert_array_equal(rd[c][:, b, :, :L], ex[c][:, b, :, :L])
+    rel = np.linalg.norm(rd["hidden"] - ex["hidden"]) / np.linalg.norm(ex["hidden"])
+    assert 2.0 ** -12 < rel < 2.0 ** -6
+    # the probability rounding alone moves attention by no more than its size
+    q = x["k_cache"][0, :, :, :WL.N].transpose(0, 2, 1, 3)        # any bf16 [B][N][H][D]
+    q = np.repeat(q, WL.Hq // WL.Hkv, axis=2)
+    kc, vc = x["k_cache"][0].copy(), x["v_cache"][0].copy()
+    for b, L in enumerate(x["seq_lens"]):
+        kc[b, :, int(L):int(L) + WL.N] = x["k_cache"][0, b, :, :WL.N]
+        vc[b, :, int(L):int(L) + WL.N] = x["v_cache"][0, b, :, :WL.N]
+    a0 = oracle.tree_attention(q, kc, vc, x["seq_lens"], x["parent"], 0.1, "bf16")
+    a1 = oracle.tree_attention(q, kc, vc, x["seq_lens"], x["parent"], 0.1, "bf16",
+                               p_round=oracle.round_bf16)
+    # |sum_t (p~_t - p_t) v_t| / sum_t p_t <= 2^-8 max |v| when |p~ - p| <= 2^-8 p
+    d = np.abs(a1 - a0)
+    vmax = np.nanmax(np.abs(oracle.decode(vc, "bf16")))
+    assert 0 < d.max() <= 2.0 ** -8 * vmax

@@ -20,4 +20,4 @@ from .gen import (  # noqa: F401
     bf16_bits_from_f32,
     BF16_QNAN,
 )
-from .model import MODELS, ModelConfig, model_inputs, model_weights  # noqa: F401
+from .model import MODEL_CASES, MODELS, ModelConfig, model_inputs, model_weights  # noqa: F401

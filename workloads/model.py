@@ -64,6 +64,33 @@ MODELS = {
                             V=1000, seed=2005),
 }
 
+
+def _model_cases():
+    from .gen import WORKLOADS
+    q8 = WORKLOADS["qwen3_8b_L1024_N64"]
+    r8 = WORKLOADS["qwen3_8b_ragged8_N64"]
+    return {
+        "tiny_d64_B2_ragged": ("tiny_d64", r8.replace(B=2, Hq=4, Hkv=2, D=64, N=12, L_lo=20,
+                                                      L_hi=70, seed=5)),
+        "small_d128_L300_N64": ("small_d128", q8.replace(Hq=8, Hkv=2, L_lo=300, L_hi=300, seed=61)),
+        "small_d128_B3_N40_M120": ("small_d128", r8.replace(B=3, Hq=8, Hkv=2, N=40, L_lo=10,
+                                                            L_hi=200, seed=62)),
+        # unsplit gate/up projection with the fused silu(gate) * up epilogue
+        "wide_mlp_N64_L200": ("wide_mlp", q8.replace(Hq=2, Hkv=1, L_lo=200, L_hi=200, seed=63)),
+        # 512 and 640 rows: the products with 256-row H tiles (the last slice
+        # of 640 rows half empty)
+        "small_d128_B8_N64_M512": ("small_d128", r8.replace(B=8, Hq=8, Hkv=2, N=64, L_lo=10,
+                                                            L_hi=120, seed=64)),
+        "small_d128_B10_N64_M640": ("small_d128", r8.replace(B=10, Hq=8, Hkv=2, N=64, L_lo=10,
+                                                             L_hi=90, seed=65)),
+        # the full Qwen3-8B-shaped stack on one 64-node tree over 1024 tokens
+        "qwen3_8b_L1024_N64": ("qwen3_8b", q8),
+    }
+
+
+# Multi-layer pass cases: name -> (model, workload).
+MODEL_CASES = _model_cases()
+
 _W_KEYS = ("embed", "ln1", "w_qkv", "q_norm", "k_norm", "w_o", "ln2", "w_gu", "w_down",
            "final_norm", "lm_head")
 
