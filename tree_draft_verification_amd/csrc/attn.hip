@@ -90,12 +90,15 @@ __device__ __forceinline__ void flag(int32_t* st, int b, int f) {
   if (st) atomicOr(&st[b], f);
 }
 
-// max(x, y) of scores that are never NaN, as the median of (x, y, +inf):
-// one v_max3 covers two of them, with none of the quieting that fmaxf's
-// NaN rules add in front of every v_max.
-__device__ __forceinline__ float smax(float x, float y) {
-  return __builtin_amdgcn_fmed3f(x, y, __builtin_inff());
+// Maxima of scores that are never NaN.  fmaxf must quiet signalling NaNs, so
+// the compiler puts a v_max(x, x) in front of every operand it cannot prove
+// canonical; v_max3_f32 written out takes three operands with no such step.
+__device__ __forceinline__ float max3f(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
 }
+__device__ __forceinline__ float smax(float x, float y) { return max3f(x, y, y); }
 
 // Reductions across the four 16-lane groups of a wavefront (lanes l, l^16,
 // l^32, l^48) with the gfx950 row/half swaps: each swap returns both
@@ -229,7 +232,7 @@ void attn_bf16_kernel(AttnArgs a) {
   __shared__ int sBT[PAGED ? kMaxPagedBlocks : 1];  // this workgroup's pages
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS addresses
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int kg = lane >> 4;
@@ -504,11 +507,12 @@ void attn_bf16_kernel(AttnArgs a) {
             s[qb][kb][r] = bit ? s[qb][kb][r] : -INFINITY;
           }
       }
-      float mk[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        mk[kb] = smax(smax(s[qb][kb][0], s[qb][kb][1]), smax(s[qb][kb][2], s[qb][kb][3]));
-      float tmax = smax(smax(mk[0], mk[1]), smax(mk[2], mk[3]));
+      const float m0 = max3f(s[qb][0][0], s[qb][0][1], s[qb][0][2]);
+      const float m1 = max3f(s[qb][0][3], s[qb][1][0], s[qb][1][1]);
+      const float m2 = max3f(s[qb][1][2], s[qb][1][3], s[qb][2][0]);
+      const float m3 = max3f(s[qb][2][1], s[qb][2][2], s[qb][2][3]);
+      const float m4 = max3f(s[qb][3][0], s[qb][3][1], s[qb][3][2]);
+      float tmax = max3f(max3f(m0, m1, m2), max3f(m3, m4, s[qb][3][3]), -INFINITY);
       tmax = max_across_groups(tmax);
       const float tm = tmax * a.scale_log2;  // scale > 0, so max commutes
       if (__any(tm > m_ref[qb] + kLazy)) {
