@@ -179,6 +179,9 @@ def main():
                     help="time draft-tree construction on this configuration")
     ap.add_argument("--compact-stack", type=int, default=0,
                     help="time layered KV compaction over this many stacked layers")
+    ap.add_argument("--compact-path-depth", type=int, default=20,
+                    help="accepted paths of this depth through level-ordered trees of width 7 "
+                         "(0: the deepest root paths of the workload's own trees)")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many bytes")
     args = ap.parse_args()
@@ -730,15 +733,30 @@ def compact_stack_bench(args):
     B, Hkv, D, Lcap, P = wl.B, wl.Hkv, wl.D, wl.Lcap, 32
     path_h = np.full((B, P), -1, dtype=np.int32)
     plen_h = np.zeros(B, dtype=np.int32)
-    for b in range(B):
-        node = int(np.argmax(depth[b]))         # deepest node, smallest index
-        chain = []
-        while node >= 0:
-            chain.append(node)
-            node = int(par[b, node])
-        chain.reverse()
-        path_h[b, :len(chain)] = chain
-        plen_h[b] = len(chain)
+    pd, pw = args.compact_path_depth, 7
+    if pd > 0:
+        # accepted paths through level-ordered trees of depth pd and width
+        # pw (the shape the level-by-level builder makes, node 0 then pw
+        # nodes per level): node j of the path is drawn from level j
+        if 1 + pd * pw > Lcap - int(lens_h.max()) or pd + 1 > P:
+            raise SystemExit("bench.py: --compact-path-depth does not fit the caches")
+        rng = np.random.default_rng(wl.seed + 7)
+        for b in range(B):
+            chain = [0] + [1 + (j - 1) * pw + int(rng.integers(pw)) for j in range(1, pd + 1)]
+            path_h[b, :len(chain)] = chain
+            plen_h[b] = len(chain)
+        tree_rows = 1 + pd * pw
+    else:
+        for b in range(B):
+            node = int(np.argmax(depth[b]))         # deepest node, smallest index
+            chain = []
+            while node >= 0:
+                chain.append(node)
+                node = int(par[b, node])
+            chain.reverse()
+            path_h[b, :len(chain)] = chain
+            plen_h[b] = len(chain)
+        tree_rows = wl.N
     moved = int(sum((path_h[b, :plen_h[b]] != np.arange(plen_h[b])).sum() for b in range(B)))
     e = 2
     nbytes = 4 * moved * Hkv * D * e * layers + 8 * B
@@ -753,7 +771,7 @@ def compact_stack_bench(args):
     for b in range(B):   # only the tree rows are read; fill them with seeded bits
         L = int(lens_h[b])
         for c in (k, v):
-            c[:, b, :, L:L + wl.N].random_(-32768, 32767, generator=g)
+            c[:, b, :, L:L + tree_rows].random_(-32768, 32767, generator=g)
     lens0 = torch.from_numpy(lens_h.astype(np.int32)).to(dev)
     lens = lens0.clone()
     path = torch.from_numpy(path_h).to(dev)
@@ -815,13 +833,13 @@ def compact_stack_bench(args):
             evc[i - args.warmup][1].record()
     torch.cuda.synchronize()
     copy_us = float(np.median([x[0].elapsed_time(x[1]) * 1e3 for x in evc]))
-    workload = f"{wl.name} geometry, {layers} stacked layers"
+    workload = (f"{wl.name} geometry, {layers} stacked layers"
+                + (f", depth-{pd} width-{pw} paths" if pd > 0 else ""))
     traffic = None
     if os.path.exists(COUNTERS):
         with open(COUNTERS) as f:
-            cnt = json.load(f).get("compact_kernel_layered", {})
-        if (cnt.get("workload") == workload
-                and cnt.get("source_digest") == kernel_source_digest(COMPACT_SOURCES)):
+            cnt = json.load(f).get(f"compact_kernel_layered/{workload}", {})
+        if cnt.get("source_digest") == kernel_source_digest(COMPACT_SOURCES):
             traffic = cnt.get("traffic_bytes")
     res = {
         "metric": "KV compaction bandwidth (tv_kv_compact_layers, one launch over stacked layers)",

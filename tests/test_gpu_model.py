@@ -192,6 +192,41 @@ def test_compact_layers_bit_exact_and_reusable(dtype):
     assert int(ws.sum()) == 0
 
 
+def test_compact_layers_many_planes_per_workgroup():
+    """64 sequences over 32 layers of 4 KV heads: eight workgroups per
+    sequence, each moving 32 planes in several rounds.  Paths whose moves
+    read rows that later moves write (path[j] = 2j), long runs of moved
+    rows, and random paths."""
+    import torch
+    import tree_draft_verification_amd as tv
+    rng = np.random.default_rng(72)
+    Ly, B, Hkv, Lcap, D, P = 32, 64, 4, 80, 64, 32
+    kc = rng.integers(0, 65535, size=(Ly, B, Hkv, Lcap, D)).astype(np.uint16)
+    vc = rng.integers(0, 65535, size=(Ly, B, Hkv, Lcap, D)).astype(np.uint16)
+    lens = rng.integers(0, 8, size=B).astype(np.int32)
+    path = np.full((B, P), -1, np.int32)
+    plen = np.zeros(B, np.int32)
+    for b in range(B):
+        if b % 3 == 0:
+            n = 32
+            path[b, :n] = np.arange(n) * 2            # every move reads a later destination
+        elif b % 3 == 1:
+            n = 32
+            path[b, :n] = np.concatenate([[0], np.arange(1, n) + 30])
+        else:
+            n = int(rng.integers(1, 33))
+            path[b, :n] = np.concatenate([[0], np.sort(rng.choice(np.arange(1, 70), n - 1, replace=False))])
+        plen[b] = n
+    k2, v2, l2 = oracle.kv_compact_layers(kc, vc, lens, path, plen)
+    k, v, sl = to_dev(kc, "bf16"), to_dev(vc, "bf16"), i32_dev(lens)
+    ws = torch.zeros(tv.tv_kv_compact_layers_workspace(B), dtype=torch.uint8, device="cuda")
+    tv.tv_kv_compact_layers(k, v, sl, i32_dev(path), i32_dev(plen), workspace=ws)
+    np.testing.assert_array_equal(to_host_bits(k), k2)
+    np.testing.assert_array_equal(to_host_bits(v), v2)
+    np.testing.assert_array_equal(sl.cpu().numpy(), l2)
+    assert int(ws.sum()) == 0
+
+
 def test_graph_replay_of_the_whole_step_matches_eager():
     """pass -> accept -> multi-layer compaction captured once and replayed;
     every replay (restored inputs, eager work in between) is bit-identical
