@@ -19,6 +19,7 @@ function to something other than itself live in tests/test_oracle_pins.py.
 from .verify import (  # noqa: F401
     ancestors,
     decode,
+    kv_commit_slots,
     kv_compact,
     kv_compact_paged,
     lm_head_argmax,

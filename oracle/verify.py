@@ -298,6 +298,36 @@ def kv_compact_paged(k_pages, v_pages, block_table, page_size, seq_lens, path, p
     return k, v, lens
 
 
+def kv_commit_slots(block_table, seq_lens, path, path_len, N: int):
+    """Commit of the accepted path on a slot table (a block table whose pages
+    hold one row each): the table entries move, not the rows.
+
+    The serving engine keeps its KV cache in pages (JetSpec GitHub README,
+    "Quick Start") and each sequence of a ragged batch keeps its own KV state
+    (EQSPEC/EXSPEC abstract).  Reading used here: with one row per page, the
+    compaction of kv_compact becomes a permutation of the table window
+    L_b .. L_b + N - 1 of each sequence.  Position L_b + j takes the slot of
+    tree node path[j] for j < path_len; the slots of the rejected nodes follow,
+    in node order, at L_b + path_len .. L_b + N - 1 (free for the next tree
+    rows, which need path_len more slots appended by the caller); seq_lens[b]
+    grows by path_len.  Returns the new table and lengths (inputs untouched).
+    """
+    bt = np.array(block_table, dtype=np.int32, copy=True)
+    lens = np.array(seq_lens, dtype=np.int32, copy=True)
+    for b in range(bt.shape[0]):
+        L = int(lens[b])
+        n = int(path_len[b])
+        window = [int(x) for x in bt[b, L:L + N]]
+        taken = [int(path[b, j]) for j in range(n)]
+        if any(not 0 <= t < N for t in taken) or any(x >= y for x, y in zip(taken, taken[1:])):
+            raise ValueError(f"path of sequence {b} is not increasing within the tree")
+        rejected = [window[i] for i in range(N) if i not in taken]
+        new = [window[i] for i in taken] + rejected
+        bt[b, L:L + N] = new
+        lens[b] = L + n
+    return bt, lens
+
+
 # ----------------------------------------------------------------------------
 # the whole step
 

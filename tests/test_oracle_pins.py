@@ -517,3 +517,78 @@ def test_paged_oracle_matches_contiguous_under_any_page_placement():
             oracle.paged_to_contiguous(k2, pg["block_table"], ps, a["Lcap"]), kc)
         np.testing.assert_array_equal(
             oracle.paged_to_contiguous(v2, pg["block_table"], ps, a["Lcap"]), vc)
+
+
+def test_commit_slots_hand_example():
+    """Sequence 0 (prefix 2, tree of 5 nodes in slots 102..106) accepts nodes
+    0, 2, 4: its window becomes the accepted slots, then the rejected ones in
+    node order; sequence 1 accepts 0, 1 and keeps its order."""
+    bt = np.arange(20, dtype=np.int32).reshape(2, 10) + 100
+    path = np.array([[0, 2, 4, -1], [0, 1, -1, -1]], np.int32)
+    nbt, lens = oracle.kv_commit_slots(bt, np.array([2, 3]), path, np.array([3, 2]), 5)
+    np.testing.assert_array_equal(nbt[0], [100, 101, 102, 104, 106, 103, 105, 107, 108, 109])
+    np.testing.assert_array_equal(nbt[1], bt[1])
+    np.testing.assert_array_equal(lens, [5, 5])
+    with pytest.raises(ValueError):
+        oracle.kv_commit_slots(bt, np.array([2, 3]), np.array([[0, 3, 2, -1], [0, 1, -1, -1]]),
+                               np.array([3, 2]), 5)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_commit_slots_equals_row_compaction(seed):
+    """With one row per page, the committed table names, at every logical row
+    below the new length, the row that the (pinned) row-moving compaction puts
+    there; the tree window is a permutation of the old one (no slot lost or
+    doubled) and nothing outside it changes."""
+    from workloads import WORKLOADS, attn_inputs, paged_layout
+    wl = WORKLOADS["qwen3_8b_ragged8_N64"].replace(B=4, L_lo=3, L_hi=60, N=24, Hq=2, Hkv=2, D=8,
+                                                   seed=80 + seed)
+    a = attn_inputs(wl)
+    pg = paged_layout(a["k_cache"], a["v_cache"], 1, seed=seed)
+    rng = np.random.default_rng(seed)
+    P = 16
+    path = np.full((wl.B, P), -1, np.int32)
+    plen = np.zeros(wl.B, np.int32)
+    for b in range(wl.B):
+        walk = oracle.ancestors(a["parent"][b], int(rng.integers(0, wl.N)))[::-1][:P]
+        path[b, :len(walk)] = walk
+        plen[b] = len(walk)
+    nbt, lens = oracle.kv_commit_slots(pg["block_table"], a["seq_lens"], path, plen, wl.N)
+    kc, vc, lc = oracle.kv_compact(a["k_cache"], a["v_cache"], a["seq_lens"], path, plen)
+    np.testing.assert_array_equal(lens, lc)
+    gk = oracle.paged_to_contiguous(pg["k_pages"], nbt, 1, a["Lcap"])
+    gv = oracle.paged_to_contiguous(pg["v_pages"], nbt, 1, a["Lcap"])
+    for b in range(wl.B):
+        n = int(lens[b])
+        np.testing.assert_array_equal(gk[b, :, :n], kc[b, :, :n])
+        np.testing.assert_array_equal(gv[b, :, :n], vc[b, :, :n])
+        L = int(a["seq_lens"][b])
+        old, new = pg["block_table"][b], nbt[b]
+        assert sorted(new[L:L + wl.N]) == sorted(old[L:L + wl.N])
+        np.testing.assert_array_equal(new[:L], old[:L])
+        np.testing.assert_array_equal(new[L + wl.N:], old[L + wl.N:])
+        # the rejected slots follow in node order
+        kept = set(int(x) for x in path[b, :plen[b]])
+        rej = [int(old[L + i]) for i in range(wl.N) if i not in kept]
+        np.testing.assert_array_equal(new[L + plen[b]:L + wl.N], rej)
+
+
+def test_commit_slots_brute_force_small_trees():
+    """Every increasing path through tiny windows (N <= 5), against a table
+    built by explicit position moves."""
+    N = 5
+    bt = np.array([[7, 11, 3, 9, 5, 13, 2, 8]], np.int32)
+    L = 2
+    for n in range(1, N + 1):
+        for rest in itertools.combinations(range(1, N), n - 1):
+            walk = (0,) + rest
+            path = np.full((1, N), -1, np.int32)
+            path[0, :n] = walk
+            nbt, lens = oracle.kv_commit_slots(bt, np.array([L]), path, np.array([n]), N)
+            want = list(bt[0])
+            window = [int(x) for x in bt[0, L:L + N]]
+            order = list(walk) + [i for i in range(N) if i not in walk]
+            for pos, node in enumerate(order):
+                want[L + pos] = window[node]
+            np.testing.assert_array_equal(nbt[0], want)
+            assert int(lens[0]) == L + n
