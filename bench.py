@@ -68,8 +68,10 @@ def kernel_source_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_work(wl, a, path, path_len):
-    """Bytes and flops each part must move / compute (not what it wastes)."""
+def algorithmic_work(wl, a, path, path_len, slots=False):
+    """Bytes and flops each part must move / compute (not what it wastes).
+    With slots (a slot table), the commit reads and writes each sequence's
+    N-entry table window and its length instead of moving rows."""
     e = 2 if wl.dtype == "bf16" else 4
     L = a["seq_lens"].astype(np.int64)
     depth = a["depth"].astype(np.int64)
@@ -80,7 +82,8 @@ def algorithmic_work(wl, a, path, path_len):
     lm_flops = int(2 * wl.M * wl.hidden * wl.V)
     moved = sum(int((path[b, :path_len[b]] != np.arange(path_len[b])).sum())
                 for b in range(wl.B))
-    compact_bytes = int(4 * moved * wl.Hkv * wl.D * e + 8 * wl.B)
+    compact_bytes = (int(8 * wl.B * wl.N + 8 * wl.B) if slots
+                     else int(4 * moved * wl.Hkv * wl.D * e + 8 * wl.B))
     accept_bytes = int(12 * wl.B * wl.N + 4 * wl.B * (path.shape[1] + 2))
     return dict(attn=(attn_bytes, attn_flops), lmhead=(lm_bytes, lm_flops),
                 accept=(accept_bytes, 0), compact=(compact_bytes, 0),
@@ -292,7 +295,10 @@ def main():
             tv.tv_tree_accept(parent, draft, argmax, P, path=path, path_len=plen, bonus=bonus)
             if events:
                 events[3].record()
-            tv.tv_kv_compact_paged(kc, vc, block_table, lens, path, plen)
+            if ps == 1:   # slot table: the commit permutes table entries, no row moves
+                tv.tv_kv_commit_slots(block_table, lens, path, plen, wl.N)
+            else:
+                tv.tv_kv_compact_paged(kc, vc, block_table, lens, path, plen)
         if events:
             events[4].record()
 
@@ -351,7 +357,7 @@ def main():
     value = wl.M * args.steps / (t1 - t0)
 
     path_h, plen_h = path.cpu().numpy(), plen.cpu().numpy()
-    work = algorithmic_work(wl, a, path_h, plen_h)
+    work = algorithmic_work(wl, a, path_h, plen_h, slots=ps == 1)
     kernels = {n: roof_entry(work[n][0], work[n][1], per[n], wl.dtype) for n in names}
 
     # Dominant kernel: the LM head (one kernel launch per call).
@@ -390,7 +396,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.B, "nodes": wl.N,
                    "prefix": [int(x) for x in a["seq_lens"]], "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "head_dim": wl.D, "hidden": wl.hidden, "vocab": wl.V,
-                   "kv_layout": f"paged{ps}" if ps else "contiguous",
+                   "kv_layout": ("slots" if ps == 1 else f"paged{ps}") if ps else "contiguous",
                    "parallelism": "none (1 GPU)"},
         "step_us": round(step_us, 2),
         "step_us_p10_p90": [round(float(np.percentile(graph_per, 10)), 2),

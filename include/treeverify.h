@@ -69,6 +69,7 @@ extern "C" {
 #define TV_STATUS_DEPTH      4 /* accepted path longer than P                */
 #define TV_STATUS_BAD_PAGE   8 /* a block-table entry outside [0, num_pages) */
 #define TV_STATUS_BAD_TOKEN 16 /* a draft token outside [0, vocab)           */
+#define TV_STATUS_BAD_PATH  32 /* path not increasing within [0, N)          */
 
 #define TV_MAX_NODES 1024 /* N limit of every call                           */
 
@@ -121,7 +122,8 @@ int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
  * block_table       [B][max_blocks] int32: logical row r of sequence b is
  *                   row r % page_size of page block_table[b][r / page_size]
  *                   (prefix rows 0..L-1, then the N tree rows L..L+N-1)
- * page_size         power of two, 16..4096; max_seq_len + N must fit in
+ * page_size         power of two, 1..4096 (1: a slot table, one row per
+ *                   page; see tv_kv_commit_slots); max_seq_len + N must fit in
  *                   max_blocks * page_size
  * workspace         at least tv_tree_verify_attn_paged_workspace() bytes
  * Device-side checks add TV_STATUS_BAD_PAGE (an entry outside the pool;
@@ -295,6 +297,31 @@ int tv_kv_compact_paged(void* k_pages, void* v_pages, const int32_t* block_table
                         int32_t* seq_lens, const int32_t* path,
                         const int32_t* path_len, int B, int Hkv, int D, int P,
                         int dtype, void* stream);
+
+/*
+ * Commit of the accepted path on a slot table: a block table whose pages
+ * hold one row each (page_size 1 in tv_tree_verify_attn_paged and
+ * tv_kv_compact_paged).  The serving engine keeps its KV cache in pages
+ * (JetSpec GitHub README, "Quick Start"); with one row per page the commit
+ * moves table entries instead of K/V rows, so no cache row is read or
+ * written.  Per sequence b, the window block_table[b][L_b .. L_b+N-1] (the
+ * tree rows) is permuted: position L_b + j takes the slot of node path[j]
+ * for j < path_len[b], and the slots of the rejected nodes follow in node
+ * order at L_b + path_len[b] .. L_b + N - 1, free for the next tree (whose N
+ * rows need path_len[b] more slots, appended by the caller).  Then
+ * seq_lens[b] += path_len[b].
+ *
+ * block_table [B][max_blocks] int32, updated in place; seq_lens [B] int32,
+ *             updated in place; path [B][P] int32 and path_len [B] int32 as
+ *             written by tv_tree_accept (path_len clamped to [0, min(P, N)]).
+ * Device-side checks (dev_status nullable): TV_STATUS_BAD_LEN (L_b < 0 or
+ * L_b + N > max_blocks), TV_STATUS_BAD_PATH (an entry outside [0, N) or not
+ * increasing); a flagged sequence is left unchanged.  Supported: 1 <= N <=
+ * TV_MAX_NODES, 1 <= P <= 64.
+ */
+int tv_kv_commit_slots(int32_t* block_table, int32_t* seq_lens, const int32_t* path,
+                       const int32_t* path_len, int B, int N, int P, int max_blocks,
+                       int32_t* dev_status, void* stream);
 
 /*
  * Multi-layer verification pass: the target model run over every node of

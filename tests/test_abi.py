@@ -42,7 +42,8 @@ def test_header_declares_the_four_calls():
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights", "tv_pack_gate_up_weights",
               "tv_accept_compact",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
-              "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
+              "tv_kv_compact_paged", "tv_kv_commit_slots", "tv_verify_pass",
+              "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
               "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_tree_build",
               "tv_tree_build_workspace", "tv_status_string", "tv_abi_version"):
@@ -195,7 +196,8 @@ def _attn_paged(lib, **kw):
 def test_paged_host_validation(lib):
     assert _attn_paged(lib, bt=None) == -1
     assert _attn_paged(lib, ps=24) == -1                 # not a power of two
-    assert _attn_paged(lib, ps=8) == -1                  # below 16 rows
+    assert _attn_paged(lib, ps=0) == -1                  # below one row
+    assert _attn_paged(lib, ps=8192) == -1               # above 4096 rows
     assert _attn_paged(lib, mb=67) == -1                 # 67 * 16 < 1024 + 64
     assert _attn_paged(lib, npg=0) == -1
     assert _attn_paged(lib, Hq=30) == -1
@@ -218,6 +220,14 @@ def test_paged_host_validation(lib):
     assert c(FAKE, FAKE, FAKE, 0, 16, 100, FAKE, FAKE, FAKE, 1, 8, 128, 32, 0, None) == -1
     assert c(FAKE, FAKE, FAKE, 68, 16, 100, FAKE, FAKE, FAKE, 1, 8, 4, 32, 0, None) == -2
     assert c(FAKE, FAKE, FAKE, 68, 16, 100, FAKE, FAKE, FAKE, 1, 8, 128, 65, 0, None) == -2
+    c = lib.tv_kv_commit_slots   # table, lens, path, path_len, B, N, P, max_blocks, status, stream
+    assert c(None, FAKE, FAKE, FAKE, 2, 64, 32, 2048, None, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, 0, 64, 32, 2048, None, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, 2, 0, 32, 2048, None, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, 2, 64, 0, 2048, None, None) == -1
+    assert c(FAKE, FAKE, FAKE, FAKE, 2, 1025, 32, 2048, None, None) == -2
+    assert c(FAKE, FAKE, FAKE, FAKE, 2, 64, 65, 2048, None, None) == -2
+    assert c(FAKE, FAKE, FAKE, FAKE, 2, 64, 32, 63, None, None) == -2
 
 
 def _pass(lib, dims=None, weights=None, **kw):
@@ -329,7 +339,8 @@ def test_binding_names_match_the_c_calls():
               "tv_lmhead_packed_bytes", "tv_lmhead_pack_weights", "tv_pack_gate_up_weights",
               "tv_accept_compact",
               "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace",
-              "tv_kv_compact_paged", "tv_verify_pass", "tv_verify_pass_workspace",
+              "tv_kv_compact_paged", "tv_kv_commit_slots", "tv_verify_pass",
+              "tv_verify_pass_workspace",
               "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "tv_graph_begin",
               "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_status_string",
               "tv_abi_version", "tv_tree_build", "tv_tree_build_workspace",

@@ -497,6 +497,14 @@ PAGED_CASES = {
     # 16-row pages and prefixes past 510 tiles: a split's block-table entries
     # cap the chunk length of the ragged plan
     "ragged2_L33500_36000_N16_ps16": ("ragged2_L33500_36000_N16", 16),
+    # slot tables (one row per page): every row through its own entry; the
+    # entries of a split cap its chunk at about 1000 rows
+    "q8_ragged3_N64_ps1": ("q8_ragged3_N64", 1),
+    "a3b_B2_L257_N200_ps1": ("a3b_B2_L257_N200", 1),
+    "empty_prefix_N20_ps1": ("empty_prefix_N20", 1),
+    "g1_L2100_N130_ps1": ("g1_L2100_N130", 1),
+    "q8_ragged8_L0_3000_N64_ps1": ("q8_ragged8_L0_3000_N64", 1),
+    "q8_bfs_L1000_N256_ps4": ("q8_bfs_L1000_N256", 4),
 }
 ATTN_CASES["ragged2_L33500_36000_N16"] = WORKLOADS["qwen3_8b_ragged8_N64"].replace(
     B=2, N=16, Hq=2, Hkv=1, L_lo=33500, L_hi=36000, seed=28)
@@ -557,7 +565,8 @@ def test_attention_paged_flags_bad_page():
 
 
 @pytest.mark.parametrize("name,ps", [("tiny_fp32", 16), ("qwen3_8b_ragged8_N64", 16),
-                                     ("qwen3_30b_a3b_B4_L4096_N1024", 64)])
+                                     ("qwen3_30b_a3b_B4_L4096_N1024", 64),
+                                     ("qwen3_8b_ragged8_N64", 1)])
 def test_compact_paged_bit_exact(name, ps):
     import tree_draft_verification_amd as tv
     wl = WORKLOADS[name]
@@ -580,6 +589,106 @@ def test_compact_paged_bit_exact(name, ps):
         gk, gv, k2, v2 = (x.view(np.uint32) for x in (gk, gv, k2, v2))
     np.testing.assert_array_equal(gk, k2)
     np.testing.assert_array_equal(gv, v2)
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_ragged8_N64", "qwen3_30b_a3b_B4_L4096_N1024",
+                                  "tiny_fp32"])
+def test_commit_slots_bit_exact(name):
+    """The committed slot table and lengths equal the oracle's, on acceptance
+    paths of the workload's trees (ragged lengths, 1024-node trees)."""
+    import tree_draft_verification_amd as tv
+    wl = WORKLOADS[name]
+    a = attn_inputs(wl.replace(Hq=wl.Hkv, D=8))   # trees and lengths only
+    Lcap = a["Lcap"]
+    rng = np.random.default_rng(46)
+    bt = np.stack([rng.permutation(wl.B * Lcap)[:Lcap] for _ in range(wl.B)]).astype(np.int32)
+    tgt = rng.integers(0, 20, size=(wl.B, wl.N)).astype(np.int32)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt)
+    acc = oracle.tree_accept(a["parent"], draft, tgt, P=32)
+    want_bt, want_lens = oracle.kv_commit_slots(bt, a["seq_lens"], acc["path"], acc["path_len"],
+                                                wl.N)
+    print(f"[commit-slots] {name} B={wl.B} N={wl.N} path_len={list(acc['path_len'])}", flush=True)
+    d_bt, lens = i32_dev(bt), i32_dev(a["seq_lens"])
+    st = i32_dev(np.zeros(wl.B, np.int32))
+    tv.tv_kv_commit_slots(d_bt, lens, i32_dev(acc["path"]), i32_dev(acc["path_len"]), wl.N,
+                          dev_status=st)
+    assert st.cpu().tolist() == [0] * wl.B
+    np.testing.assert_array_equal(d_bt.cpu().numpy(), want_bt)
+    np.testing.assert_array_equal(lens.cpu().numpy(), want_lens)
+
+
+def test_commit_slots_flags_bad_paths_and_lengths():
+    """A path that is not increasing within the tree, or a window past the
+    table, flags its sequence and leaves it unchanged; the others commit."""
+    import tree_draft_verification_amd as tv
+    B, N, P, mb = 4, 16, 8, 40
+    rng = np.random.default_rng(47)
+    bt = rng.permutation(B * mb).reshape(B, mb).astype(np.int32)
+    lens = np.array([3, 5, 30, 2], np.int32)          # sequence 2: 30 + 16 > 40
+    path = np.full((B, P), -1, np.int32)
+    plen = np.array([3, 3, 2, 4], np.int32)
+    path[0, :3] = [0, 4, 9]
+    path[1, :3] = [0, 7, 7]                            # not increasing
+    path[2, :2] = [0, 1]
+    path[3, :4] = [0, 2, 16, 17]                       # past the tree
+    st = i32_dev(np.zeros(B, np.int32))
+    d_bt, d_lens = i32_dev(bt), i32_dev(lens)
+    tv.tv_kv_commit_slots(d_bt, d_lens, i32_dev(path), i32_dev(plen), N, dev_status=st)
+    assert st.cpu().tolist() == [0, tv.TV_STATUS_BAD_PATH, tv.TV_STATUS_BAD_LEN,
+                                 tv.TV_STATUS_BAD_PATH]
+    want_bt, want_lens = oracle.kv_commit_slots(bt[:1], lens[:1], path[:1], plen[:1], N)
+    got_bt, got_lens = d_bt.cpu().numpy(), d_lens.cpu().numpy()
+    np.testing.assert_array_equal(got_bt[0], want_bt[0])
+    np.testing.assert_array_equal(got_bt[1:], bt[1:])
+    np.testing.assert_array_equal(got_lens, [want_lens[0], 5, 30, 2])
+
+
+def test_slot_table_step_reads_the_committed_rows():
+    """A step on slot tables: attention through the table, acceptance on the
+    GPU, the commit as a table permutation; the rows the committed table
+    names equal the row-moving compaction's rows, and a second attention
+    (the next step's prefixes) through the new table equals the oracle's."""
+    import tree_draft_verification_amd as tv
+    wl = ATTN_CASES["q8_ragged3_N64"]
+    a = attn_inputs(wl)
+    pg = paged_layout(a["k_cache"], a["v_cache"], 1, seed=48)
+    kp, vp, bt = _paged_dev(pg, "bf16")
+    lens = i32_dev(a["seq_lens"])
+    par = i32_dev(a["parent"])
+    msl = int(a["seq_lens"].max())
+    tv.tv_tree_verify_attn_paged(to_dev(a["q"], "bf16"), kp, vp, bt, lens, par,
+                                 max_seq_len=msl, scale=a["scale"])
+    rng = np.random.default_rng(49)
+    tgt = rng.integers(0, 20, size=(wl.B, wl.N)).astype(np.int32)
+    draft = draft_tokens(a["parent"], draft_coins(wl, a["depth"]), tgt)
+    P = 32
+    path = i32_dev(np.zeros((wl.B, P), np.int32))
+    plen = i32_dev(np.zeros(wl.B, np.int32))
+    bonus = i32_dev(np.zeros(wl.B, np.int32))
+    tv.tv_tree_accept(par, i32_dev(draft), i32_dev(tgt), P, path=path, path_len=plen, bonus=bonus)
+    tv.tv_kv_commit_slots(bt, lens, path, plen, wl.N)
+    acc = oracle.tree_accept(a["parent"], draft, tgt, P=P)
+    kc, vc, lc = oracle.kv_compact(a["k_cache"], a["v_cache"], a["seq_lens"], acc["path"],
+                                   acc["path_len"])
+    np.testing.assert_array_equal(lens.cpu().numpy(), lc)
+    new_bt = bt.cpu().numpy()
+    gk = oracle.paged_to_contiguous(pg["k_pages"], new_bt, 1, a["Lcap"])
+    gv = oracle.paged_to_contiguous(pg["v_pages"], new_bt, 1, a["Lcap"])
+    for b in range(wl.B):
+        n = int(lc[b])
+        np.testing.assert_array_equal(gk[b, :, :n], kc[b, :, :n])
+        np.testing.assert_array_equal(gv[b, :, :n], vc[b, :, :n])
+    # the next step: prefixes of the new lengths, trees on the rows after
+    # them (the caller's slots for those rows: the rejected ones, then fresh
+    # ones past the tree window, as laid out by the pool)
+    n_next = 8
+    par2 = np.tile(np.arange(-1, n_next - 1, dtype=np.int32), (wl.B, 1))
+    q2 = a["q"][:, :n_next]
+    out = tv.tv_tree_verify_attn_paged(to_dev(q2, "bf16"), kp, vp, bt, lens, i32_dev(par2),
+                                       max_seq_len=int(lc.max()), scale=a["scale"])
+    ref = oracle.tree_attention_paged(q2, pg["k_pages"], pg["v_pages"], new_bt, 1, lc, par2,
+                                      a["scale"], "bf16")
+    assert_attn_close(to_host_f64(out), ref, "slot-table next step")
 
 
 def test_compact_paged_hazard_rows_cross_pages():

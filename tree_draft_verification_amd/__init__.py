@@ -24,7 +24,7 @@ import torch
 from . import _lib
 from ._lib import (TV_BF16, TV_F32, TV_LAYOUT_PACKED, TV_LAYOUT_ROWMAJOR,  # noqa: F401
                    TV_MAX_NODES, TV_STATUS_BAD_LEN, TV_STATUS_BAD_PAGE, TV_STATUS_BAD_PARENT,
-                   TV_STATUS_BAD_TOKEN, TV_STATUS_DEPTH)
+                   TV_STATUS_BAD_PATH, TV_STATUS_BAD_TOKEN, TV_STATUS_DEPTH)
 
 _LIB_HANDLE = None
 
@@ -42,6 +42,7 @@ __all__ = [
     "tv_lmhead_pack_weights", "tv_pack_gate_up_weights", "PackedWeights", "tv_tree_accept",
     "tv_kv_compact", "tv_accept_compact", "tv_status_string", "tv_abi_version", "library_path",
     "tv_tree_verify_attn_paged", "tv_tree_verify_attn_paged_workspace", "tv_kv_compact_paged",
+    "tv_kv_commit_slots",
     "Model", "tv_model_pack", "tv_verify_pass", "tv_verify_pass_workspace",
     "tv_kv_compact_layers", "tv_kv_compact_layers_workspace", "Graph", "tv_graph_begin",
     "tv_graph_end", "tv_graph_launch", "tv_graph_destroy", "tv_tree_build",
@@ -377,6 +378,23 @@ def tv_kv_compact_paged(k_pages, v_pages, block_table, seq_lens, path, path_len)
         _ptr(k_pages), _ptr(v_pages), _ptr(block_table), max_blocks, page_size, num_pages,
         _ptr(seq_lens), _ptr(path), _ptr(path_len), B, Hkv, D, P, dt, _stream(k_pages.device))
     _check("tv_kv_compact_paged", st)
+
+
+def tv_kv_commit_slots(block_table, seq_lens, path, path_len, N: int, dev_status=None) -> None:
+    """Commit on a slot table (one row per page): permutes each sequence's
+    tree window of the table and advances the lengths; no K/V row moves."""
+    B, max_blocks = block_table.shape
+    _i32(block_table, (B, max_blocks), "block_table")
+    _i32(seq_lens, (B,), "seq_lens")
+    P = path.shape[1]
+    _i32(path, (B, P), "path")
+    _i32(path_len, (B,), "path_len")
+    if dev_status is not None:
+        _i32(dev_status, (B,), "dev_status")
+    st = _lib_handle().tv_kv_commit_slots(
+        _ptr(block_table), _ptr(seq_lens), _ptr(path), _ptr(path_len), B, int(N), P, max_blocks,
+        _ptr(dev_status) if dev_status is not None else None, _stream(block_table.device))
+    _check("tv_kv_commit_slots", st)
 
 
 # ---------------------------------------------------------------- multi-layer pass

@@ -12,6 +12,7 @@ TV_BF16, TV_F32 = 0, 1
 TV_LAYOUT_ROWMAJOR, TV_LAYOUT_PACKED = 0, 1
 TV_STATUS_BAD_PARENT, TV_STATUS_BAD_LEN, TV_STATUS_DEPTH, TV_STATUS_BAD_PAGE = 1, 2, 4, 8
 TV_STATUS_BAD_TOKEN = 16
+TV_STATUS_BAD_PATH = 32
 TV_MAX_NODES = 1024
 
 _p = ctypes.c_void_p
@@ -43,6 +44,7 @@ SIGNATURES = {
     "tv_tree_verify_attn_paged": (_i, [_p, _p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i,
                                        _i, _i, _f, _i, _p, _sz, _p, _p]),
     "tv_kv_compact_paged": (_i, [_p, _p, _p, _i, _i, _i, _p, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "tv_kv_commit_slots": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _p, _p]),
     "tv_lmhead_argmax_workspace": (_sz, [_i, _i, _i, _i]),
     "tv_lmhead_argmax": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
     "tv_lmhead_argmax_noalloc": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p]),

@@ -90,7 +90,7 @@ int tv_tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                                          static_cast<hipStream_t>(stream)));
 }
 
-static bool page_size_ok(int ps) { return ps >= 16 && ps <= 4096 && (ps & (ps - 1)) == 0; }
+static bool page_size_ok(int ps) { return ps >= 1 && ps <= 4096 && (ps & (ps - 1)) == 0; }
 
 size_t tv_tree_verify_attn_paged_workspace(int B, int N, int Hq, int Hkv, int D,
                                            int max_seq_len, int page_size, int dtype) {
@@ -143,6 +143,18 @@ int tv_kv_compact_paged(void* k_pages, void* v_pages, const int32_t* block_table
   return hip_status(tv::launch_kv_compact(k_pages, v_pages, seq_lens, path, path_len, B, Hkv, D,
                                           0, P, dtype, static_cast<hipStream_t>(stream),
                                           block_table, max_blocks, page_size, num_pages));
+}
+
+int tv_kv_commit_slots(int32_t* block_table, int32_t* seq_lens, const int32_t* path,
+                       const int32_t* path_len, int B, int N, int P, int max_blocks,
+                       int32_t* dev_status, void* stream) {
+  if (!block_table || !seq_lens || !path || !path_len) return TV_EINVAL;
+  if (B < 1 || N < 1 || P < 1 || max_blocks < 1) return TV_EINVAL;
+  if (N > TV_MAX_NODES || P > 64 || N > max_blocks) return TV_ENOTSUP;
+  if (B > 65535) return TV_ENOTSUP;
+  return hip_status(tv::launch_kv_commit_slots(block_table, seq_lens, path, path_len, B, N, P,
+                                               max_blocks, dev_status,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 size_t tv_lmhead_argmax_workspace(int M, int K, int V, int dtype) {

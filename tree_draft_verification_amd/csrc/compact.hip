@@ -208,6 +208,65 @@ __global__ __launch_bounds__(kThreads, (PAGED || ACCEPT) ? 4 : 8) void compact_k
   }
 }
 
+// Commit on a slot table (one row per page): the tree window of the table
+// is permuted, no row moves.  One workgroup per sequence, thread i for tree
+// node i: node path[j] goes to position j, a rejected node i to path_len +
+// (i minus the accepted nodes below i), counted by a binary search of the
+// increasing path.  Every entry of the window is read before the barrier and
+// written after it, so the in-place permutation needs no staging beyond one
+// register per thread.
+__global__ __launch_bounds__(TV_MAX_NODES) void commit_slots_kernel(
+    int32_t* __restrict__ table, int32_t* __restrict__ seq_lens, const int32_t* __restrict__ path,
+    const int32_t* __restrict__ path_len, int N, int P, int max_blocks,
+    int32_t* __restrict__ dev_status) {
+  __shared__ int s_path[64];
+  __shared__ int s_bad;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int L = seq_lens[b];
+  int n = path_len[b];
+  n = n < 0 ? 0 : (n > P ? P : n);
+  n = n > N ? N : n;
+  if (L < 0 || (long long)L + N > max_blocks) {
+    if (tid == 0 && dev_status != nullptr) atomicOr(&dev_status[b], TV_STATUS_BAD_LEN);
+    return;
+  }
+  if (tid < 64) {
+    // the path is increasing within [0, N): each entry checks itself and its
+    // predecessor (from the lane below)
+    const int pj = tid < n ? path[(size_t)b * P + tid] : 0x7fffffff;
+    const int prev = __shfl_up(pj, 1, 64);
+    const bool bad = tid < n && (pj < 0 || pj >= N || (tid > 0 && prev >= pj));
+    const unsigned long long any_bad = __ballot(bad);
+    s_path[tid] = pj;
+    if (tid == 0) s_bad = any_bad != 0ull;
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0 && dev_status != nullptr) atomicOr(&dev_status[b], TV_STATUS_BAD_PATH);
+    return;
+  }
+  int32_t* win = table + (size_t)b * max_blocks + L;
+  int slot = 0, dest = 0;
+  if (tid < N) {
+    slot = win[tid];
+    // accepted nodes below tid: entries of the increasing path that are < tid
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_path[mid] < tid) lo = mid + 1;
+      else hi = mid;
+    }
+    dest = (lo < n && s_path[lo] == tid) ? lo : n + (tid - lo);
+  }
+  // every entry of the window has been read (each thread waits for its own
+  // load, then the barrier) before any is written
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid < N) win[dest] = slot;
+  if (tid == 0) seq_lens[b] = L + n;
+}
+
 }  // namespace
 
 hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t* path,
@@ -267,6 +326,14 @@ hipError_t launch_accept_compact(const int32_t* parent, const int32_t* draft,
   hipLaunchKernelGGL((compact_kernel<false, true>), dim3(B), dim3(kThreads), 0, stream,
                      static_cast<char*>(k), static_cast<char*>(v), seq_lens, path, path_len, Hkv,
                      Lcap, P, row_bytes, pa, 1, 0LL, 1, nullptr, ac);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_commit_slots(int32_t* block_table, int32_t* seq_lens, const int32_t* path,
+                                  const int32_t* path_len, int B, int N, int P, int max_blocks,
+                                  int32_t* dev_status, hipStream_t stream) {
+  hipLaunchKernelGGL(commit_slots_kernel, dim3(B), dim3(TV_MAX_NODES), 0, stream, block_table,
+                     seq_lens, path, path_len, N, P, max_blocks, dev_status);
   return hipGetLastError();
 }
 

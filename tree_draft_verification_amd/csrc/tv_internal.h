@@ -131,6 +131,9 @@ hipError_t launch_tree_accept(const int32_t* parent, const int32_t* draft,
                               int32_t* bonus, int B, int N, int P,
                               int32_t* dev_status, hipStream_t stream);
 
+hipError_t launch_kv_commit_slots(int32_t* block_table, int32_t* seq_lens, const int32_t* path,
+                                  const int32_t* path_len, int B, int N, int P, int max_blocks,
+                                  int32_t* dev_status, hipStream_t stream);
 hipError_t launch_kv_compact(void* k, void* v, int32_t* seq_lens, const int32_t* path,
                              const int32_t* path_len, int B, int Hkv, int D,
                              int Lcap, int P, int dtype, hipStream_t stream,
