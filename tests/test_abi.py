@@ -209,11 +209,11 @@ def test_paged_host_validation(lib):
     assert _attn_paged(lib, ws=None) == -3
     assert _attn_paged(lib, wsb=need - 1) == -3
     assert lib.tv_tree_verify_attn_paged_workspace(1, 64, 32, 8, 128, 1024, 12, 0) == 0
-    # a long prefix with small pages is split so that one split's page
-    # entries fit the workgroup's cache: more splits than the contiguous plan
+    # pages look up their entries per row, so the split plan (and the
+    # workspace) does not depend on the page size
     long_c = lib.tv_tree_verify_attn_workspace(1, 64, 32, 8, 128, 1 << 20, 0)
-    long_p = lib.tv_tree_verify_attn_paged_workspace(1, 64, 32, 8, 128, 1 << 20, 16, 0)
-    assert long_p > long_c > 0
+    for ps in (1, 16, 4096):
+        assert lib.tv_tree_verify_attn_paged_workspace(1, 64, 32, 8, 128, 1 << 20, ps, 0) == long_c > 0
     c = lib.tv_kv_compact_paged
     assert c(None, FAKE, FAKE, 68, 16, 100, FAKE, FAKE, FAKE, 1, 8, 128, 32, 0, None) == -1
     assert c(FAKE, FAKE, FAKE, 68, 20, 100, FAKE, FAKE, FAKE, 1, 8, 128, 32, 0, None) == -1

@@ -494,11 +494,10 @@ PAGED_CASES = {
     "q8_ragged2_L2000_3100_N64_ps16": ("q8_ragged2_L2000_3100_N64", 16),
     "g1_L2100_N130_ps64": ("g1_L2100_N130", 64),
     "q8_ragged8_L0_3000_N64_ps16": ("q8_ragged8_L0_3000_N64", 16),
-    # 16-row pages and prefixes past 510 tiles: a split's block-table entries
-    # cap the chunk length of the ragged plan
+    # 16-row pages and prefixes past 510 tiles (long splits of the ragged
+    # plan, every row through its page entry)
     "ragged2_L33500_36000_N16_ps16": ("ragged2_L33500_36000_N16", 16),
-    # slot tables (one row per page): every row through its own entry; the
-    # entries of a split cap its chunk at about 1000 rows
+    # slot tables (one row per page): every row through its own entry
     "q8_ragged3_N64_ps1": ("q8_ragged3_N64", 1),
     "a3b_B2_L257_N200_ps1": ("a3b_B2_L257_N200", 1),
     "empty_prefix_N20_ps1": ("empty_prefix_N20", 1),

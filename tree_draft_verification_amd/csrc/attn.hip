@@ -76,7 +76,7 @@ struct AttnArgs {
   int nqblk, nsplit, chunk_len, total_blocks;
   // ragged batches: per-sequence splits derived on the device from the
   // lengths (ragged_plan); nsplit and chunk_len above are then unused
-  int ragged, want_blocks, min_tiles, max_chunk_tiles;
+  int ragged, want_blocks, min_tiles;
   int* ragged_start;  // [B + 1] (ragged): workgroup 0 publishes the plan here for the combine
   int anc_words;   // ceil(N / 64)
   float scale_log2;  // scale * log2(e)
@@ -126,7 +126,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Prefix splits of a ragged batch (at most kMaxRaggedB sequences), derived
 // from the lengths so that every split holds about the same number of key
 // tiles whatever the mix of lengths: chunk = max(min_tiles, ceil(total tiles
-// x Hkv x query blocks / want_blocks)) tiles (at most max_chunk_tiles),
+// x Hkv x query blocks / want_blocks)) tiles,
 // nsplit_b = max(1, ceil(tiles_b / chunk)), and every sequence with more
 // than one split gets one more for its tree keys while the whole grid stays
 // within want_blocks.  Work items (b, split) are numbered sequence by
@@ -165,14 +165,12 @@ __device__ RaggedPlan ragged_plan(const AttnArgs& a) {
       for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off, 64);
       return (long)n;
     };
-    // the smallest chunk (at least the even share, min_tiles and at most
-    // max_chunk_tiles) whose items fit the workgroup target: the per-sequence
-    // rounding up must not push the grid into a second round
+    // the smallest chunk (at least the even share and min_tiles) whose items
+    // fit the workgroup target: the per-sequence rounding up must not push
+    // the grid into a second round
     long ct = ((long)total * hq + a.want_blocks - 1) / a.want_blocks;
     if (ct < a.min_tiles) ct = a.min_tiles;
     long hi = most > ct ? most : ct;
-    if (hi > a.max_chunk_tiles) hi = a.max_chunk_tiles;
-    if (ct > hi) ct = hi;
     while (ct < hi && items_at(ct) * hq > a.want_blocks) {  // non-increasing in ct
       const long mid = (ct + hi) / 2;
       if (items_at(mid) * hq <= a.want_blocks) hi = mid;
@@ -229,7 +227,6 @@ void attn_bf16_kernel(AttnArgs a) {
   unsigned long long* const sAnc = kDma ? sAncDyn : sAncStatic;
   __shared__ unsigned sTreeMask;
   __shared__ int8_t sTreeList[TV_MAX_NODES / 64];
-  __shared__ int sBT[PAGED ? kMaxPagedBlocks : 1];  // this workgroup's pages
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar LDS addresses
@@ -323,36 +320,26 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- where key/value rows live: one contiguous plane per (sequence, KV
-  // head), or pages of a pool named by the block table.  For pages, the
-  // entries of the prefix chunk and of the tree rows are cached in LDS once
-  // (published by the first barrier of the tile loop).
+  // head), or pages of a pool named by the block table.  For pages, the lanes
+  // that load a row look up its page entry themselves (a 4-byte load; a
+  // sequence's entries are read by all its query blocks, so they sit in L2):
+  // no entries are staged in LDS, so neither the page size nor the length of
+  // a split is bounded by LDS.  An entry outside the pool reads page 0 and
+  // flags TV_STATUS_BAD_PAGE at the end.
   const size_t kv_plane = ((size_t)b * a.Hkv + g) * (size_t)a.Lcap * D;
   const int sh = a.page_shift;
-  const int pre_blk0 = c0 >> sh;
-  const int n_pre_blk = PAGED && c1 > c0 ? ((c1 - 1) >> sh) - pre_blk0 + 1 : 0;
-  const int tree_blk0 = L >> sh;
-  if constexpr (PAGED) {
-    const int n_tree_blk = do_tree ? ((L + N - 1) >> sh) - tree_blk0 + 1 : 0;
-    const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
-    int bad = 0;
-    for (int i = tid; i < n_pre_blk + n_tree_blk; i += kThreads) {
-      const int blk = i < n_pre_blk ? pre_blk0 + i : tree_blk0 + (i - n_pre_blk);
-      int pg = bt[blk];
-      if (pg < 0 || pg >= a.num_pages) {
-        bad = 1;
+  const int32_t* bt = PAGED ? a.block_table + (size_t)b * a.max_blocks : nullptr;
+  int bad_page = 0;
+  auto row_off = [&](int row, bool tree) -> size_t {
+    (void)tree;
+    if constexpr (PAGED) {
+      int pg = bt[row >> sh];
+      if ((unsigned)pg >= (unsigned)a.num_pages) {
+        bad_page = 1;
         pg = 0;
       }
-      sBT[i] = pg;
-    }
-    if (bad) flag(a.dev_status, b, TV_STATUS_BAD_PAGE);
-  }
-  auto row_off = [&](int row, bool tree) -> size_t {
-    if constexpr (PAGED) {
-      const int blk = row >> sh;
-      const int pg = sBT[tree ? n_pre_blk + blk - tree_blk0 : blk - pre_blk0];
       return ((((size_t)pg * a.Hkv + g) << sh) + (row & ((1 << sh) - 1))) * D;
     } else {
-      (void)tree;
       return kv_plane + (size_t)row * D;
     }
   };
@@ -679,6 +666,10 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (PAGED) {
+    if (bad_page) flag(a.dev_status, b, TV_STATUS_BAD_PAGE);
+  }
+
   // ---- epilogue: lane holds O^T rows d = db*16 + 4*kg + r of its query
 #pragma unroll
   for (int qb = 0; qb < QBW; ++qb) {
@@ -906,17 +897,7 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dt
       p.nsplit = (ntiles + per - 1) / per;
     }
   }
-  if (dtype == TV_BF16 && page_size > 0 && ntiles > 0) {
-    // the block-table entries of one split and of the tree rows live in LDS
-    const int tree_blk = N / page_size + 2;
-    const long max_rows = (long)(kMaxPagedBlocks - tree_blk - 2) * page_size;
-    const long max_tiles = max_rows / kKT > 0 ? max_rows / kKT : 1;
-    if (p.chunk_len / kKT > max_tiles) {
-      const int per = (int)max_tiles;
-      p.chunk_len = per * kKT;
-      p.nsplit = (ntiles + per - 1) / per;
-    }
-  }
+  (void)page_size;  // pages look up their entries per row: the plan is the contiguous one
   // With the prefix split, the tree keys get a split of their own (the last,
   // whose prefix range is empty) while the grid stays within the target:
   // otherwise the workgroup that owns the last prefix chunk also walks the
@@ -939,16 +920,7 @@ AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dt
     p.ragged = 1;
     p.want_blocks = (int)want_blocks;
     p.min_tiles = min_tiles;
-    p.max_chunk_tiles = 1 << 30;
-    long max_items = want_blocks / hq + 1 + 2L * B;
-    if (page_size > 0) {
-      const int tree_blk = N / page_size + 2;
-      const long max_rows = (long)(kMaxPagedBlocks - tree_blk - 2) * page_size;
-      const long max_tiles = max_rows / kKT > 0 ? max_rows / kKT : 1;
-      p.max_chunk_tiles = (int)(max_tiles < (1 << 30) ? max_tiles : (1 << 30));
-      max_items += (long)B * ((ntiles + max_tiles - 1) / max_tiles);
-    }
-    p.max_items = (int)max_items;
+    p.max_items = (int)(want_blocks / hq + 1 + 2L * B);
   }
   p.ws_bytes = 0;
   if (p.ragged) {
@@ -999,7 +971,6 @@ hipError_t launch_tree_attn(const void* q, const void* k, const void* v,
   a.ragged = plan.ragged;
   a.want_blocks = plan.want_blocks;
   a.min_tiles = plan.min_tiles;
-  a.max_chunk_tiles = plan.max_chunk_tiles;
   a.total_blocks = plan.ragged ? plan.max_items * Hkv * plan.nqblk
                                : B * Hkv * plan.nqblk * plan.nsplit;
   a.anc_words = (N + 63) / 64;

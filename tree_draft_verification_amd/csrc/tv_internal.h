@@ -84,15 +84,13 @@ struct AttnPlan {
   int nsplit;     // workgroups along the prefix per query block
   int chunk_len;  // prefix keys per split (multiple of 64)
   // ragged batches: splits derived on the device from the lengths
-  int ragged, want_blocks, min_tiles, max_chunk_tiles, max_items;
+  int ragged, want_blocks, min_tiles, max_items;
   size_t ws_bytes;
 };
 
 // Largest batch whose splits are derived on the device from its lengths.
 constexpr int kMaxRaggedBatch = 64;
 
-// Block-table entries a tree-attention workgroup caches in LDS (paged caches).
-constexpr int kMaxPagedBlocks = 2048;
 
 // page_size 0 = contiguous caches
 AttnPlan attn_plan(int B, int N, int Hq, int Hkv, int D, int max_seq_len, int dtype,
