@@ -90,6 +90,25 @@ def algorithmic_work(wl, a, path, path_len, slots=False):
                 accept_compact=(accept_bytes + compact_bytes, 0))
 
 
+def lmhead_kernel_name(M, V, dtype):
+    """Name of the kernel the library runs for the LM head at these sizes
+    (the label only; it follows the library's host-side choice: the
+    streaming kernel up to 64 rows, the eight-wavefront product from 256
+    rows with the 384-row W tile where its rounds of 256 workgroups cost
+    less)."""
+    if dtype != "bf16":
+        return "lmhead_f32_kernel"
+    if M <= 64:
+        return "lmhead_stream_kernel (packed W)"
+    if M >= 256:
+        nmt = -(-M // 256)
+        r256 = -(-(nmt * -(-V // 256)) // 256)
+        r384 = -(-(nmt * -(-V // 384)) // 256)
+        tw = 384 if r384 * 1.5 * 0.95 < r256 else 256
+        return f"gemm8_argmax_kernel<{tw}> + argmax_reduce_kernel"
+    return "gemm32_kernel + argmax_reduce_kernel"
+
+
 def roof_entry(nbytes, flops, us, dtype):
     t = us * 1e-6
     gbs = nbytes / t / 1e9
@@ -379,13 +398,7 @@ def main():
         achieved = lm_b / (lm_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic)
-    if wl.dtype != "bf16":
-        lm_kernel = "lmhead_f32_kernel"
-    elif wl.M <= 64:
-        lm_kernel = "lmhead_stream_kernel (packed W)"
-    else:
-        lm_kernel = ("gemm32w_kernel" if wl.M >= 512 else "gemm32_kernel") + " + argmax_reduce_kernel"
-    roof.update(kernel=lm_kernel,
+    roof.update(kernel=lmhead_kernel_name(wl.M, wl.V, wl.dtype),
                 algorithmic_bytes=lm_b, launch_us=round(lm_us, 2))
 
     res = {

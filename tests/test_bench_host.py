@@ -66,3 +66,13 @@ def test_algorithmic_work_of_the_default_workload():
     assert w["attn"][1] == 4 * 32 * 128 * int((4096 + depth + 1).sum())
     # compaction: K and V rows read and written for each moved row, lengths in and out
     assert w["compact"][0] == 4 * 6 * 4 * 128 * 2 + 8 * 4
+
+
+def test_lmhead_kernel_label_follows_the_library_choice():
+    """The labels the profiles show for each workload's LM head."""
+    b = _bench()
+    assert b.lmhead_kernel_name(4096, 151936, "bf16") == "gemm8_argmax_kernel<384> + argmax_reduce_kernel"
+    assert b.lmhead_kernel_name(512, 151936, "bf16") == "gemm8_argmax_kernel<256> + argmax_reduce_kernel"
+    assert b.lmhead_kernel_name(256, 151936, "bf16") == "gemm8_argmax_kernel<384> + argmax_reduce_kernel"
+    assert b.lmhead_kernel_name(64, 151936, "bf16") == "lmhead_stream_kernel (packed W)"
+    assert b.lmhead_kernel_name(7, 1000, "f32") == "lmhead_f32_kernel"
