@@ -527,24 +527,49 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
   // acc[i][j][e]: W row v0 + TW/4 wv + 32 i + 8 (e / 4) + 4 hh + e % 4,
   // H row m0 + 128 wh + 32 j + r32.  Every read of the stages is done (the
   // loop ends at a barrier), so the key table can take the first W stage.
+  // Per row, a lane first takes the maximum of its 16 BW candidates, then the
+  // first candidate (in increasing vocabulary order: i, then e) equal to it;
+  // the index and the 64-bit key are formed once per row.  Only the last W
+  // tile checks indices against V, with a strict compare in increasing order
+  // that keeps the first of equal maxima.
+  constexpr int NC = 16 * BW;
   KeyRow* s_key = reinterpret_cast<KeyRow*>(sW0);
   const int vw0 = vt * TW + wv * (TW / NWV);
+  const bool full = vw0 + TW / NWV <= V;
+  auto pos_v = [&](int pos) { return vw0 + 32 * (pos >> 4) + 8 * ((pos & 15) >> 2) + 4 * hh + (pos & 3); };
 #pragma unroll
   for (int j = 0; j < BH; ++j) {
     const int hrow = wh * (TH / NWH) + 32 * j + r32;
     const int m = m0 + hrow;
-    unsigned long long best = 0ull;
+    float bv = -INFINITY;
+    int bp = -1;
+    if (full) {
+      bv = acc[0][j][0];
 #pragma unroll
-    for (int i = 0; i < BW; ++i)
+      for (int pos = 1; pos + 1 < NC; pos += 2)
+        bv = fmaxf(fmaxf(bv, acc[pos >> 4][j][pos & 15]), acc[(pos + 1) >> 4][j][(pos + 1) & 15]);
+      if (NC % 2 == 0) bv = fmaxf(bv, acc[BW - 1][j][15]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int v = vw0 + 32 * i + 8 * (e >> 2) + 4 * hh + (e & 3);
-        if (v < V) {
-          const unsigned long long key = argmax_key(acc[i][j][e], (uint32_t)v);
-          best = key > best ? key : best;
-          if (logits != nullptr && m < M) logits[(size_t)m * V + v] = acc[i][j][e];
-        }
+      for (int pos = NC - 1; pos >= 0; --pos) bp = acc[pos >> 4][j][pos & 15] == bv ? pos : bp;
+    } else {
+#pragma unroll
+      for (int pos = 0; pos < NC; ++pos) {
+        const float x = acc[pos >> 4][j][pos & 15];
+        const bool take = pos_v(pos) < V && x > bv;
+        bv = take ? x : bv;
+        bp = take ? pos : bp;
       }
+    }
+    if (logits != nullptr && m < M) {
+#pragma unroll
+      for (int i = 0; i < BW; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int v = pos_v(16 * i + e);
+          if (v < V) logits[(size_t)m * V + v] = acc[i][j][e];
+        }
+    }
+    unsigned long long best = bp >= 0 ? argmax_key(bv, (uint32_t)pos_v(bp)) : 0ull;
     const unsigned long long o = shfl_xor_u64(best, 32);
     best = o > best ? o : best;
     if (hh == 0) s_key[wv][hrow] = best;

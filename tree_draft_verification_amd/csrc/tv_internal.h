@@ -70,9 +70,9 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
 }
 
 // Packed (value, index) key: the maximum key is the largest value, and among
-// equal values the smallest index.
+// equal values (-0 and +0 included: f + 0 is +0 for both) the smallest index.
 __device__ __forceinline__ unsigned long long argmax_key(float f, uint32_t idx) {
-  return ((unsigned long long)f32_order_key(f) << 32) | (unsigned long long)(~idx);
+  return ((unsigned long long)f32_order_key(f + 0.0f) << 32) | (unsigned long long)(~idx);
 }
 
 // ---------------------------------------------------------------- launchers
