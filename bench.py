@@ -90,22 +90,44 @@ def algorithmic_work(wl, a, path, path_len, slots=False):
                 accept_compact=(accept_bytes + compact_bytes, 0))
 
 
+def gemm8_plan(M, V):
+    """W tiles of each width (384-row tiles first, then 256-row ones) that the
+    library's LM head takes from 256 rows on: the split with the fewest rounds
+    of 256 workgroups, a 384-row round counting 1.425 of a 256-row one and a
+    second launch 0.05; on equal cost the most 384-row tiles."""
+    nmt = -(-M // 256)
+
+    def rounds(t):
+        return -(-(nmt * t) // 256)
+
+    best, cost = (0, -(-V // 256)), rounds(-(-V // 256))
+    a = -(-V // 384)
+    if rounds(a) * 1.425 < cost:
+        best, cost = (a, 0), rounds(a) * 1.425
+    n = 1
+    while 384 * n < V:
+        tail = -(-(V - 384 * n) // 256)
+        c = rounds(n) * 1.425 + rounds(tail) + 0.05
+        if c <= cost:
+            best, cost = (n, tail), c
+        n += 1
+    return best
+
+
 def lmhead_kernel_name(M, V, dtype):
     """Name of the kernel the library runs for the LM head at these sizes
     (the label only; it follows the library's host-side choice: the
     streaming kernel up to 64 rows, the eight-wavefront product from 256
-    rows with the 384-row W tile where its rounds of 256 workgroups cost
-    less)."""
+    rows, in one or two launches by W tile width as gemm8_plan splits the
+    vocabulary)."""
     if dtype != "bf16":
         return "lmhead_f32_kernel"
     if M <= 64:
         return "lmhead_stream_kernel (packed W)"
     if M >= 256:
-        nmt = -(-M // 256)
-        r256 = -(-(nmt * -(-V // 256)) // 256)
-        r384 = -(-(nmt * -(-V // 384)) // 256)
-        tw = 384 if r384 * 1.5 * 0.95 < r256 else 256
-        return f"gemm8_argmax_kernel<{tw}> + argmax_reduce_kernel"
+        n384, n256 = gemm8_plan(M, V)
+        names = (["gemm8_argmax_kernel<384>"] if n384 else []) + (["gemm8_argmax_kernel<256>"] if n256 else [])
+        return " + ".join(names + ["argmax_reduce_kernel"])
     return "gemm32_kernel + argmax_reduce_kernel"
 
 

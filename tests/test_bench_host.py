@@ -71,8 +71,30 @@ def test_algorithmic_work_of_the_default_workload():
 def test_lmhead_kernel_label_follows_the_library_choice():
     """The labels the profiles show for each workload's LM head."""
     b = _bench()
+    both = "gemm8_argmax_kernel<384> + gemm8_argmax_kernel<256> + argmax_reduce_kernel"
     assert b.lmhead_kernel_name(4096, 151936, "bf16") == "gemm8_argmax_kernel<384> + argmax_reduce_kernel"
-    assert b.lmhead_kernel_name(512, 151936, "bf16") == "gemm8_argmax_kernel<256> + argmax_reduce_kernel"
-    assert b.lmhead_kernel_name(256, 151936, "bf16") == "gemm8_argmax_kernel<384> + argmax_reduce_kernel"
+    assert b.lmhead_kernel_name(512, 151936, "bf16") == both
+    assert b.lmhead_kernel_name(256, 151936, "bf16") == both
+    assert b.lmhead_kernel_name(256, 4163, "bf16") == "gemm8_argmax_kernel<256> + argmax_reduce_kernel"
     assert b.lmhead_kernel_name(64, 151936, "bf16") == "lmhead_stream_kernel (packed W)"
     assert b.lmhead_kernel_name(7, 1000, "f32") == "lmhead_f32_kernel"
+
+
+def test_lmhead_tile_plan():
+    """The split of the vocabulary into 384-row then 256-row W tiles: every
+    row covered once, the 384-row run whole when a tail follows, and the
+    rounds of 256 workgroups it saves at the workloads' sizes."""
+    b = _bench()
+    # one H slice: 256 tiles of 384 (one round) + 210 of 256 (one round)
+    # instead of 396 tiles of 384 (two rounds)
+    assert b.gemm8_plan(256, 151936) == (256, 210)
+    assert b.gemm8_plan(4096, 151936) == (396, 0)     # 24.75 rounds: one width
+    assert b.gemm8_plan(300, 66000) == (128, 66)
+    assert b.gemm8_plan(256, 4163) == (0, 17)
+    for M in (256, 300, 512, 1000, 2048, 4096):
+        for V in (1000, 4163, 66000, 151936, 152064):
+            n384, n256 = b.gemm8_plan(M, V)
+            if n256:
+                assert 384 * n384 < V <= 384 * n384 + 256 * n256 < V + 256
+            else:
+                assert V <= 384 * n384 < V + 384

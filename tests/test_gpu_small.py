@@ -178,9 +178,12 @@ LM_CASES = {
     "M64_K256_V151936": Q8.replace(N=64, hidden=256, V=151936, seed=37),
     # ragged last tile (33 rows) after 781 whole ones
     "M17_K512_V100001": Q8.replace(B=1, N=17, hidden=512, V=100001, seed=38),
-    # the eight-wavefront product with its 384-row W tile (chosen: 2 rounds of
-    # 344 workgroups against 3 of 516), a partial last W tile and H slice
+    # the eight-wavefront product: 128 W tiles of 384 rows (one round of 256
+    # workgroups), then 66 of 256 rows with a partial last one, and a partial
+    # last H slice
     "M300_K256_V66000": Q8.replace(B=1, N=300, hidden=256, V=66000, seed=39),
+    # one width: 17 W tiles of 256 rows
+    "M256_K256_V4163": Q8.replace(N=256, hidden=256, V=4163, seed=40),
 }
 
 
@@ -301,6 +304,29 @@ def test_lmhead_stream_kernel_ties_across_its_tiles():
     for wt in (wd, tv.tv_lmhead_pack_weights(wd)):
         arg = tv.tv_lmhead_argmax(to_dev(h, "bf16"), wt).cpu().numpy()
         np.testing.assert_array_equal(arg, want)
+
+
+def test_lmhead_ties_across_the_two_tile_widths():
+    """From 256 rows the vocabulary is split into 384-row then 256-row W
+    tiles, launched separately: duplicate W rows in the first tile, the last
+    384-row tile, the 256-row tail and its partial last tile tie exactly at
+    the maximum; the smallest index wins."""
+    import tree_draft_verification_amd as tv
+    from workloads import bf16_bits_from_f32
+    rng = np.random.default_rng(41)
+    M, K, V = 300, 256, 66000          # 128 tiles of 384 rows, then 66 of 256
+    Hi = rng.integers(1, 3, size=(M, K)).astype(np.float32)
+    Wi = rng.integers(-1, 2, size=(V, K)).astype(np.float32)
+    for dup in ([49151, 49152, 65999], [65999, 50000], [11, 65999, 49151]):
+        Wd = Wi.copy()
+        Wd[dup] = 1.0
+        exact = Hi.astype(np.int64) @ Wd.T.astype(np.int64)
+        want = np.argmax(exact, axis=1)
+        assert (want == min(dup)).all()
+        wd = to_dev(bf16_bits_from_f32(Wd), "bf16")
+        arg = tv.tv_lmhead_argmax(to_dev(bf16_bits_from_f32(Hi), "bf16"),
+                                  tv.tv_lmhead_pack_weights(wd)).cpu().numpy()
+        np.testing.assert_array_equal(arg, want, err_msg=f"duplicates at {dup}")
 
 
 def test_lmhead_cached_workspaces_of_mixed_dtypes_and_sizes():

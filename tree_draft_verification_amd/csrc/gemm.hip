@@ -411,7 +411,8 @@ template <int TW>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
                          unsigned long long* __restrict__ keys, float* __restrict__ logits, int M,
-                         int K, int V, int nmt, int total_blocks) {
+                         int K, int V, int nmt, int total_blocks, int v_base, int key_base,
+                         int nkeys) {
   constexpr int KC = 64;           // k per stage
   constexpr int TH = 256;
   constexpr int NWAVE = 8;
@@ -454,7 +455,7 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < DMA_W; ++i) {
       const int s0 = 2 * (wave * DMA_W + i);  // even: both halves in one packed tile
-      int pt = (TW / kPT) * vt + (s0 >> 5);
+      int pt = v_base / kPT + (TW / kPT) * vt + (s0 >> 5);
       pt = pt < ntp ? pt : ntp - 1;           // past the last tile: read it, drop the rows
       const uint32_t off = ((uint32_t)pt * nk128 * 32 + (s0 & 31)) * 64 + wc + wlane;
       __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)off * 8),
@@ -531,12 +532,15 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
   // first candidate (in increasing vocabulary order: i, then e) equal to it;
   // the index and the 64-bit key are formed once per row.  Only the last W
   // tile checks indices against V, with a strict compare in increasing order
-  // that keeps the first of equal maxima.
+  // that keeps the first of equal maxima.  Candidate pos = 16 i + e is row
+  // vw0 + 4 hh + voff(pos) (voff a compile-time constant), in range while
+  // voff(pos) < lim.
   constexpr int NC = 16 * BW;
   KeyRow* s_key = reinterpret_cast<KeyRow*>(sW0);
-  const int vw0 = vt * TW + wv * (TW / NWV);
+  const int vw0 = v_base + vt * TW + wv * (TW / NWV);
   const bool full = vw0 + TW / NWV <= V;
-  auto pos_v = [&](int pos) { return vw0 + 32 * (pos >> 4) + 8 * ((pos & 15) >> 2) + 4 * hh + (pos & 3); };
+  const int lim = V - vw0 - 4 * hh;
+  auto voff = [](int pos) { return 32 * (pos >> 4) + 8 * ((pos & 15) >> 2) + (pos & 3); };
 #pragma unroll
   for (int j = 0; j < BH; ++j) {
     const int hrow = wh * (TH / NWH) + 32 * j + r32;
@@ -555,21 +559,18 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
 #pragma unroll
       for (int pos = 0; pos < NC; ++pos) {
         const float x = acc[pos >> 4][j][pos & 15];
-        const bool take = pos_v(pos) < V && x > bv;
+        const bool take = voff(pos) < lim && x > bv;
         bv = take ? x : bv;
         bp = take ? pos : bp;
       }
     }
     if (logits != nullptr && m < M) {
+      float* lrow = logits + (size_t)m * V + vw0 + 4 * hh;
 #pragma unroll
-      for (int i = 0; i < BW; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int v = pos_v(16 * i + e);
-          if (v < V) logits[(size_t)m * V + v] = acc[i][j][e];
-        }
+      for (int pos = 0; pos < NC; ++pos)
+        if (voff(pos) < lim) lrow[voff(pos)] = acc[pos >> 4][j][pos & 15];
     }
-    unsigned long long best = bp >= 0 ? argmax_key(bv, (uint32_t)pos_v(bp)) : 0ull;
+    unsigned long long best = bp >= 0 ? argmax_key(bv, (uint32_t)(vw0 + 4 * hh + voff(bp))) : 0ull;
     const unsigned long long o = shfl_xor_u64(best, 32);
     best = o > best ? o : best;
     if (hh == 0) s_key[wv][hrow] = best;
@@ -580,7 +581,7 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
     unsigned long long k = s_key[0][r];
 #pragma unroll
     for (int w = 1; w < NWV; ++w) k = s_key[w][r] > k ? s_key[w][r] : k;
-    keys[(size_t)(m0 + r) * nvt + vt] = k;
+    keys[(size_t)(m0 + r) * nkeys + key_base + vt] = k;
   }
 }
 
@@ -591,21 +592,44 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
 // against 11.2 ms of projections).
 bool use_wide(int M) { return M >= kWideRows; }
 
-// The eight-wavefront LM head from this many rows on, and its W tile.  One
-// workgroup fits a CU, so the grid runs in rounds of 256 workgroups: the
-// 384-row tile (about 5 % cheaper per product, 1.5x the work per
-// workgroup) is taken when its rounds cost less.  Measured: 256 rows
-// (594 -> 396 workgroups, 3 -> 2 rounds) 393 -> 380 us; 512 rows (1188 ->
-// 792, 5 -> 4 rounds of 1.5x work) 636 -> 687 us, so 256 there; 4096 rows
-// 2238-2326 -> 2225 us.
+// The eight-wavefront LM head from this many rows on, and its W tiles.  One
+// workgroup fits a CU, so a launch runs in rounds of 256 workgroups, and a
+// round costs what its longest workgroup costs.  The vocabulary is split
+// into a run of 384-row W tiles (about 5 % cheaper per product, 1.5x the
+// work per workgroup) and a tail of 256-row tiles, in two launches, where
+// that takes fewer rounds than one width alone: at 256 H rows and 151936
+// vocabulary rows, 256 tiles of 384 rows (one round) and 210 of 256 rows
+// (one round of two-thirds the work) against 396 tiles of 384 (two
+// rounds).  Measured with one width: 256 rows (594 -> 396 workgroups, 3 ->
+// 2 rounds) 393 -> 380 us; 512 rows (1188 -> 792, 5 -> 4 rounds of 1.5x
+// work) 636 -> 687 us; 4096 rows 2238-2326 -> 2225 us.
 constexpr int kGemm8Rows = 256;
 constexpr int kCUs = 256;
 bool use_gemm8(int M) { return M >= kGemm8Rows; }
-int gemm8_tile(int M, int V) {
+struct Gemm8Plan {
+  int n384, n256;  // W tiles of each width: rows [0, 384 n384) then the rest
+};
+Gemm8Plan gemm8_plan(int M, int V) {
   const long nmt = (M + 255) / 256;
-  const long r256 = (nmt * ((V + 255) / 256) + kCUs - 1) / kCUs;
-  const long r384 = (nmt * ((V + 383) / 384) + kCUs - 1) / kCUs;
-  return r384 * 1.5 * 0.95 < (double)r256 ? 384 : 256;
+  auto rounds = [&](long tiles) { return (nmt * tiles + kCUs - 1) / kCUs; };
+  // cost in rounds of 256-row tiles; a second launch adds a little
+  constexpr double k384 = 1.5 * 0.95, kLaunch = 0.05;
+  Gemm8Plan best{0, (V + 255) / 256};
+  double cost = (double)rounds(best.n256);
+  const int all384 = (V + 383) / 384;
+  if (rounds(all384) * k384 < cost) {
+    best = Gemm8Plan{all384, 0};
+    cost = rounds(all384) * k384;
+  }
+  for (int n = 1; 384L * n < V; ++n) {  // on equal cost, the most 384-row tiles
+    const int tail = (V - 384 * n + 255) / 256;
+    const double c = rounds(n) * k384 + rounds(tail) + kLaunch;
+    if (c <= cost) {
+      best = Gemm8Plan{n, tail};
+      cost = c;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -613,8 +637,11 @@ int gemm8_tile(int M, int V) {
 int gemm32_vtiles(int V) { return (V + kWT - 1) / kWT; }
 
 int gemm_argmax_vtiles(int M, int V) {
-  const int tw = use_gemm8(M) ? gemm8_tile(M, V) : kWT;
-  return (V + tw - 1) / tw;
+  if (use_gemm8(M)) {
+    const Gemm8Plan p = gemm8_plan(M, V);
+    return p.n384 + p.n256;
+  }
+  return (V + kWT - 1) / kWT;
 }
 
 int gemm32_splits(int M, int K, int Nout) {
@@ -631,15 +658,22 @@ hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
                                 hipStream_t stream) {
   if (use_gemm8(M)) {
     const int nmt = (M + 255) / 256;
-    const int total = nmt * gemm_argmax_vtiles(M, V);
-    if (gemm8_tile(M, V) == 384)
-      hipLaunchKernelGGL(gemm8_argmax_kernel<384>, dim3(total), dim3(512), 0, stream,
-                         static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed),
-                         keys, logits, M, K, V, nmt, total);
-    else
-      hipLaunchKernelGGL(gemm8_argmax_kernel<256>, dim3(total), dim3(512), 0, stream,
-                         static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed),
-                         keys, logits, M, K, V, nmt, total);
+    const Gemm8Plan p = gemm8_plan(M, V);
+    const int nkeys = p.n384 + p.n256;
+    const bf16_t* h = static_cast<const bf16_t*>(hidden);
+    const bf16_t* w = static_cast<const bf16_t*>(w_packed);
+    if (p.n384 > 0) {
+      const int total = nmt * p.n384;
+      hipLaunchKernelGGL(gemm8_argmax_kernel<384>, dim3(total), dim3(512), 0, stream, h, w, keys,
+                         logits, M, K, V, nmt, total, 0, 0, nkeys);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (p.n256 > 0) {
+      const int total = nmt * p.n256;
+      hipLaunchKernelGGL(gemm8_argmax_kernel<256>, dim3(total), dim3(512), 0, stream, h, w, keys,
+                         logits, M, K, V, nmt, total, 384 * p.n384, p.n384, nkeys);
+    }
     return hipGetLastError();
   }
   const int rows = use_wide(M) ? 256 : 128;
