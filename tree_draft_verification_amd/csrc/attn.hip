@@ -452,17 +452,22 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int ks = 0; ks < DS; ++ks) kf[kb][ks].u = kfrag(kb, ks);
-    // S^T = K Q^T: lane holds query column l16, keys kb*16 + 4*kg + r.
+    // S^T = K Q^T: lane holds query column l16, keys kb*16 + 4*kg + r.  The
+    // k step is the outer loop (and in O^T += V^T P^T below the key half u), so
+    // eight independent products separate two into one accumulator and the
+    // second half's exponentials can run under the first half's products;
+    // each accumulator still sums in the same order.
     f32x4_t s[QBW][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < DS; ++ks)
+    for (int ks = 0; ks < DS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = mfma16x16x32(kf[kb][ks].v, qf[qb][ks], s[qb][kb]);
-    }
     // O^T += V^T P^T below reads these (the first half of the output rows'
     // fragments are in flight during the softmax, the second half during the
     // first half's products); k-slot e of lane group kg is key 32u + 4kg + e
@@ -533,9 +538,9 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) vf[db][u].u = vfrag(db, u);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) o[qb][db] = mfma16x16x32(vf[db][u].v, pf[qb][u].v, o[qb][db]);
   };
