@@ -495,8 +495,10 @@ void attn_bf16_kernel(AttnArgs a) {
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t bit = ((kb < 2 ? wlo : whi) >> ((kb & 1) * 16 + r)) & 1u;
-            s[qb][kb][r] = bit ? s[qb][kb][r] : -INFINITY;
+            // all ones where the key is visible: the score, else -inf
+            const uint32_t keep =
+                (uint32_t)__builtin_amdgcn_sbfe((int)(kb < 2 ? wlo : whi), (kb & 1) * 16 + r, 1);
+            s[qb][kb][r] = __uint_as_float((__float_as_uint(s[qb][kb][r]) & keep) | (~keep & 0xff800000u));
           }
       }
       const float m0 = max3f(s[qb][0][0], s[qb][0][1], s[qb][0][2]);
@@ -504,10 +506,12 @@ void attn_bf16_kernel(AttnArgs a) {
       const float m2 = max3f(s[qb][1][2], s[qb][1][3], s[qb][2][0]);
       const float m3 = max3f(s[qb][2][1], s[qb][2][2], s[qb][2][3]);
       const float m4 = max3f(s[qb][3][0], s[qb][3][1], s[qb][3][2]);
-      float tmax = max3f(max3f(m0, m1, m2), max3f(m3, m4, s[qb][3][3]), -INFINITY);
-      tmax = max_across_groups(tmax);
-      const float tm = tmax * a.scale_log2;  // scale > 0, so max commutes
-      if (__any(tm > m_ref[qb] + kLazy)) {
+      const float lmax = max3f(max3f(m0, m1, m2), max3f(m3, m4, s[qb][3][3]), -INFINITY);
+      // a query's tile maximum exceeds the threshold exactly when one of its
+      // four lane groups' maxima does, so the maximum across the groups is
+      // only formed for a rescale
+      if (__any(lmax * a.scale_log2 > m_ref[qb] + kLazy)) {
+        const float tm = max_across_groups(lmax) * a.scale_log2;
         const float m_new = smax(m_ref[qb], tm);
         const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_ref[qb] - m_new);
         l_run[qb] *= alpha;
