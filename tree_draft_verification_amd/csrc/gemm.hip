@@ -407,12 +407,16 @@ void gemm32w_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
 // the first W stage) and 256 VGPRs; it reads 17 % fewer operand bytes per
 // product and 22 % fewer fragments per matrix instruction than the 256-row
 // tile, which measured 4-5 % faster on the 4096 x 2048 x 151936 product.
-template <int TW>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
-                         unsigned long long* __restrict__ keys, float* __restrict__ logits, int M,
-                         int K, int V, int nmt, int total_blocks, int v_base, int key_base,
-                         int nkeys) {
+// Store mode (the projections of the multi-layer pass from 256 rows): a
+// workgroup owns one k range of nsplit and writes its fp32 partial sums
+// part[split][M][V]; the splits of a tile share a die.
+template <int TW, int MODE>
+__device__ __forceinline__ void gemm8_body(const bf16_t* __restrict__ H,
+                                           const bf16_t* __restrict__ W,
+                                           unsigned long long* __restrict__ keys,
+                                           float* __restrict__ logits, float* __restrict__ part,
+                                           int M, int K, int V, int nmt, int nsplit,
+                                           int total_blocks, int v_base, int key_base, int nkeys) {
   constexpr int KC = 64;           // k per stage
   constexpr int TH = 256;
   constexpr int NWAVE = 8;
@@ -432,13 +436,16 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int r32 = lane & 31, hh = lane >> 5;
   const int wv = wave / NWH, wh = wave % NWH;
-  // which (H slice, W tile): groups of mg H slices per W tile on one die
-  const int nvt = total_blocks / nmt;
+  // which (H slice, k split, W tile): logical order (mi, ks, vt, group), so
+  // groups of mg H slices and the splits of one W tile run on one die
+  const int nvt = total_blocks / (nmt * nsplit);
   const int lid = xcd_remap(blockIdx.x, total_blocks);
   const int mg = nmt % 4 == 0 ? 4 : (nmt % 2 == 0 ? 2 : 1);
   const int r1 = lid / mg;
-  const int vt = r1 % nvt;
-  const int m0 = ((r1 / nvt) * mg + lid % mg) * TH;
+  const int ks = r1 % nsplit;
+  const int r2 = r1 / nsplit;
+  const int vt = r2 % nvt;
+  const int m0 = ((r2 / nvt) * mg + lid % mg) * TH;
   const int nk128 = K / 128;
   const int ntp = (V + kPT - 1) / kPT;  // packed 128-row tiles
 
@@ -492,8 +499,11 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = K / KC;
-  dma(sW0, sH0, 0);
+  // chunks [cb, cb + nkl) of this split, whole pairs (one per stage)
+  const int npair = K / (2 * KC);
+  const int cb = 2 * (ks * npair / nsplit);
+  const int nkl = 2 * ((ks + 1) * npair / nsplit) - cb;
+  dma(sW0, sH0, cb);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __builtin_amdgcn_s_barrier();
   // chunk c on stage U (compile-time: each stage one known LDS object); the
@@ -503,7 +513,7 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
     constexpr int U = decltype(stage_tag)::value;
     const bf16_t* sw = U ? sW1 : sW0;
     const bf16_t* sh = U ? sH1 : sH0;
-    dma(U ? sW0 : sW1, U ? sH0 : sH1, min(c + 1, nk - 1));
+    dma(U ? sW0 : sW1, U ? sH0 : sH1, min(c + 1, cb + nkl - 1));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < KC / 16; ++t) {
@@ -520,7 +530,7 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_s_barrier();
   };
-  for (int c0 = 0; c0 < nk; c0 += 2) {
+  for (int c0 = cb; c0 < cb + nkl; c0 += 2) {
     chunk(c0, std::integral_constant<int, 0>{});
     chunk(c0 + 1, std::integral_constant<int, 1>{});
   }
@@ -528,6 +538,32 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
   // acc[i][j][e]: W row v0 + TW/4 wv + 32 i + 8 (e / 4) + 4 hh + e % 4,
   // H row m0 + 128 wh + 32 j + r32.  Every read of the stages is done (the
   // loop ends at a barrier), so the key table can take the first W stage.
+  if constexpr (MODE == kGemmStore) {
+    // lane: rows m0 + 128 wh + 32 j + r32, W rows vw0 + 32 i + 8 q + 4 hh .. + 3
+    const int vw0 = v_base + vt * TW + wv * (TW / NWV) + 4 * hh;
+#pragma unroll
+    for (int j = 0; j < BH; ++j) {
+      const int m = m0 + wh * (TH / NWH) + 32 * j + r32;
+      if (m >= M) continue;
+      float* dst = part + ((size_t)ks * M + m) * V + vw0;
+#pragma unroll
+      for (int i = 0; i < BW; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int v = vw0 + 32 * i + 8 * q;
+          const f32x4_t val = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                               acc[i][j][4 * q + 3]};
+          if ((V & 3) == 0 && v + 3 < V) {
+            *reinterpret_cast<f32x4_t*>(dst + 32 * i + 8 * q) = val;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (v + e < V) dst[32 * i + 8 * q + e] = val[e];
+          }
+        }
+    }
+    return;
+  }
   // Per row, a lane first takes the maximum of its 16 BW candidates, then the
   // first candidate (in increasing vocabulary order: i, then e) equal to it;
   // the index and the 64-bit key are formed once per row.  Only the last W
@@ -585,6 +621,25 @@ void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict_
   }
 }
 
+template <int TW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm8_argmax_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
+                         unsigned long long* __restrict__ keys, float* __restrict__ logits, int M,
+                         int K, int V, int nmt, int total_blocks, int v_base, int key_base,
+                         int nkeys) {
+  gemm8_body<TW, kGemmArgmax>(H, W, keys, logits, nullptr, M, K, V, nmt, 1, total_blocks, v_base,
+                              key_base, nkeys);
+}
+
+template <int TW>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm8_store_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
+                        float* __restrict__ part, int M, int K, int Nout, int nmt, int nsplit,
+                        int total_blocks) {
+  gemm8_body<TW, kGemmStore>(H, W, nullptr, nullptr, part, M, K, Nout, nmt, nsplit, total_blocks,
+                             0, 0, 0);
+}
+
 // The 256-row tile serves the LM head (one pass over k, argmax epilogue).
 // The split-K projections stay on 128-row tiles: with half as many tiles
 // they would take twice the splits, each with half the k range and twice
@@ -632,6 +687,36 @@ Gemm8Plan gemm8_plan(int M, int V) {
   return best;
 }
 
+// The store-mode product from 256 rows (the multi-layer pass's projections):
+// the W tile width and the k split with the least modelled time, rounds of
+// 256 workgroups x (chunks per split + 2 for the ramp and the epilogue) x
+// 1.8 us per 256-row chunk (1.425x for 384 rows), plus the partial sums
+// written and read back at 5 TB/s.
+struct Gemm8StorePlan {
+  int tw, nsplit;
+};
+Gemm8StorePlan gemm8_store_plan(int M, int K, int Nout) {
+  const long nmt = (M + 255) / 256;
+  const int npair = K / 128;
+  Gemm8StorePlan best{256, 1};
+  double cost = 1e300;
+  for (int tw = 256; tw <= 384; tw += 128) {
+    const long nvt = (Nout + tw - 1) / tw;
+    const double unit = tw == 384 ? 1.425 : 1.0;
+    for (int s = 1; s <= npair; ++s) {
+      if (npair % s) continue;
+      const long rounds = (nmt * nvt * s + kCUs - 1) / kCUs;
+      const double t = rounds * (2.0 * npair / s + 2) * unit * 1.8 +
+                       (double)s * M * Nout * 8 / 5e6;
+      if (t < cost) {
+        cost = t;
+        best = Gemm8StorePlan{tw, s};
+      }
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 int gemm32_vtiles(int V) { return (V + kWT - 1) / kWT; }
@@ -645,6 +730,7 @@ int gemm_argmax_vtiles(int M, int V) {
 }
 
 int gemm32_splits(int M, int K, int Nout) {
+  if (use_gemm8(M) && K % 128 == 0) return gemm8_store_plan(M, K, Nout).nsplit;
   const int tiles = ((M + 127) / 128) * gemm32_vtiles(Nout);
   const int npair = K / (2 * kKC);
   int best = 1;
@@ -692,6 +778,20 @@ hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
 
 hipError_t launch_gemm32_store(const void* hidden, const void* w_packed, float* part, int M,
                                int K, int Nout, int nsplit, hipStream_t stream) {
+  if (use_gemm8(M) && K % 128 == 0) {
+    const int nmt = (M + 255) / 256;
+    const int tw = gemm8_store_plan(M, K, Nout).tw;
+    const int total = nmt * ((Nout + tw - 1) / tw) * nsplit;
+    const bf16_t* h = static_cast<const bf16_t*>(hidden);
+    const bf16_t* w = static_cast<const bf16_t*>(w_packed);
+    if (tw == 384)
+      hipLaunchKernelGGL(gemm8_store_kernel<384>, dim3(total), dim3(512), 0, stream, h, w, part, M,
+                         K, Nout, nmt, nsplit, total);
+    else
+      hipLaunchKernelGGL(gemm8_store_kernel<256>, dim3(total), dim3(512), 0, stream, h, w, part, M,
+                         K, Nout, nmt, nsplit, total);
+    return hipGetLastError();
+  }
   const int nmt = (M + 127) / 128;
   const int total = nmt * gemm32_vtiles(Nout) * nsplit;
   hipLaunchKernelGGL(gemm32_kernel<kGemmStore>, dim3(total), dim3(kThreads), 0, stream,
