@@ -53,6 +53,8 @@ BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 FP32_VEC_TFLOPS = 157.3
 METRIC = "verified tree nodes/s + verify-step µs on 1 MI355X; % of HBM/MFMA roofline"
 DEFAULT_WORKLOAD = "qwen3_30b_a3b_B4_L4096_N1024"
+# (multi-layer pass, decode loop) workloads of each synthetic model's geometry
+MODEL_WORKLOADS = {"qwen3_8b": ("qwen3_8b_L1024_N64", "qwen3_8b_ragged8_N64")}
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 LMHEAD_SOURCES = [os.path.join(ROOT, "tree_draft_verification_amd", "csrc", f)
                   for f in ("lmhead.hip", "gemm.hip", "tv_internal.h")]
@@ -208,7 +210,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help=f"workload (default {DEFAULT_WORKLOAD}; with --model, the model's own: "
+                         "its 64-node step for the pass, its ragged batch for --decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paged", type=int, default=0,
                     help="page size of a paged key/value cache (0: contiguous caches)")
@@ -236,6 +240,15 @@ def main():
     if args.calibrate_copy:
         copy_calibration(args.calibrate_copy)
         return
+    if args.workload is None:
+        if args.model:
+            if args.model not in MODEL_WORKLOADS:
+                print(f"bench.py: --model {args.model} needs a --workload of its attention geometry",
+                      file=sys.stderr)
+                sys.exit(2)
+            args.workload = MODEL_WORKLOADS[args.model][1 if args.decode else 0]
+        else:
+            args.workload = DEFAULT_WORKLOAD
     if args.model and args.decode:
         decode_bench(args)
         return

@@ -4,26 +4,25 @@
 // by argmax_reduce_kernel) and by the projections of the multi-layer pass
 // (split-K partial sums, finished by the epilogue kernels).  At these sizes
 // the product is bound by the matrix cores, not by reading W, so the tiling
-// is built around operand reuse:
-//   * v_mfma_f32_32x32x16_bf16: a 32 x 32 block per instruction, half the
-//     operand bytes per flop of the 16 x 16 form;
-//   * a workgroup owns 256 W rows and 128 or 256 H rows; each of its 4
-//     wavefronts owns 64 W rows (two 32-row blocks) against all of the H
-//     rows, 128 or 256 fp32 accumulators per lane;
-//   * W comes from the packed layout (the LM head's) straight into MFMA
-//     operand registers through a two-chunk ring, each W byte read by one
-//     wavefront; H is staged through double-buffered LDS and read by all
-//     four;
+// is built around operand reuse (v_mfma_f32_32x32x16_bf16: a 32 x 32 block
+// per instruction, half the operand bytes per flop of the 16 x 16 form):
+//   * below 256 rows, gemm32_kernel: a workgroup of 4 wavefronts owns 256 W
+//     rows and 128 H rows; each wavefront owns 64 W rows against all of the
+//     H rows (128 accumulators per lane); W comes from the packed layout (the
+//     LM head's) straight into MFMA operand registers through a two-chunk
+//     ring, each W byte read by one wavefront; H is staged through
+//     double-buffered LDS and read by all four;
+//   * from 256 rows, the eight-wavefront kernels (gemm8_argmax_kernel for
+//     the LM head, gemm8_store_kernel for the projections): 256 H rows and
+//     256 or 384 W rows per workgroup, both operands copied from memory
+//     straight into LDS;
 //   * workgroups that share a W tile (up to four H slices) get adjacent
 //     logical ids, which the remap places on one die, so the tile comes from
 //     HBM once per die and the slices' rows stay in its L2.
-// What bounds it is the rate at which a compute unit's vector memory path
+// What bounds them is the rate at which a compute unit's vector memory path
 // brings chunks in from L2 (about 74 cache lines in flight per CU, ~500
-// cycles each).  For the LM head from 512 rows on, a 256-row H tile halves
-// the H bytes per product and runs 6-14 % faster; it has no registers left
-// for staging H, so H goes straight from memory into LDS.  At 256 rows it
-// would leave most CUs with two tiles against three, and the split-K
-// projections would need twice the splits, so both keep the 128-row tile.
+// cycles each), so the lever is bytes per product: the larger tiles of the
+// eight-wavefront kernels.
 // Operand lane layout of the 32 x 32 x 16 form (measured): lane l holds
 // row (or column) l % 32 and k values 8*(l/32) .. 8*(l/32)+7; result
 // register i of lane l is row 8*(i/4) + 4*(l/32) + i%4, column l % 32.
@@ -41,7 +40,6 @@ constexpr int kWT = 256;        // W rows per workgroup
 constexpr int kPT = 128;        // W rows per packed tile
 constexpr int kKC = 128;        // k per pipeline stage (8 steps of 16)
 constexpr int kHRow = kKC + 8;  // LDS row of the register-staged H stage (bf16); 272 bytes
-constexpr int kWideRows = 512;  // the 256-row H tile from this many rows on
 
 enum : int { kGemmArgmax = 0, kGemmStore = 1 };
 
@@ -269,122 +267,6 @@ void gemm32_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
       for (int i = 0; i < kHP; ++i) *reinterpret_cast<u32x4_t*>(&sH[u ^ 1][hdst[i]]) = hreg[i];
       __syncthreads();
     }
-  }
-  epilogue<MODE, MT>(acc, tl, s_key, keys, logits, part, M, V);
-}
-
-// 256 H rows per workgroup; H goes straight from memory into LDS (no
-// registers are left for staging it next to 256 accumulators per lane).
-template <int MODE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
-void gemm32w_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__ W,
-                    unsigned long long* __restrict__ keys, float* __restrict__ logits,
-                    float* __restrict__ part, int M, int K, int V, int nmt, int nsplit,
-                    int total_blocks) {
-  constexpr int MT = 256;
-  constexpr int kDI = MT / 16;  // direct-to-LDS loads per wavefront per stage
-  // Two stages as separate arrays, so that the reads of one never wait for
-  // the loads filling the other.  Rows of 256 bytes; 16-byte piece x of row
-  // r sits at position x ^ (r & 15), which keeps the fragment reads free of
-  // bank conflicts.
-  __shared__ __attribute__((aligned(1024))) bf16_t sH0[MT * kKC];
-  __shared__ __attribute__((aligned(1024))) bf16_t sH1[MT * kKC];
-  __shared__ unsigned long long s_key[4][MT];
-
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int r32 = lane & 31;
-  const int hh = lane >> 5;
-  const Tile tl = tile_of(total_blocks, nmt, nsplit, MT, K, V, wave);
-  const int cb = tl.cb, nkl = tl.nkl;
-  auto wload = [&](int c, int b, int t) -> u32x4_t {
-    return *reinterpret_cast<const u32x4_t*>(W + w_offset(tl, r32, hh, c, b, t));
-  };
-
-  // Wavefront w fills stage rows 64w .. 64w+63, four rows (1 KB) per
-  // instruction: lane p of instruction i brings row 64w + 4i + p/16, piece
-  // (p % 16) ^ (row & 15).  Rows past M read row M - 1.  Offsets are taken
-  // from the slice's first row (at most 256 rows of K elements).
-  const bf16_t* hslice = H + (size_t)tl.m0 * K;
-  int hoff[kDI];
-#pragma unroll
-  for (int i = 0; i < kDI; ++i) {
-    const int row = 64 * wave + 4 * i + (lane >> 4);
-    const int x = (lane & 15) ^ (row & 15);
-    const int rl = tl.m0 + row < M ? row : M - 1 - tl.m0;
-    hoff[i] = rl * K + 8 * x;
-  }
-  auto hdma = [&](bf16_t* stage, int c) {
-#pragma unroll
-    for (int i = 0; i < kDI; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(hslice + hoff[i] + (size_t)c * kKC),
-          (__attribute__((address_space(3))) void*)(stage + (64 * wave + 4 * i) * kKC), 16, 0, 0);
-  };
-  // fragment of 32-row block mb, k step t: row 32mb + r32, piece 2t + hh
-  auto frag = [&](const bf16_t* stage, int mb, int t) -> bf16x8_t {
-    const int pos = (2 * t + hh) ^ (r32 & 15);
-    Frag8 f;
-    f.q = *reinterpret_cast<const u32x4_t*>(stage + (mb * 32 + r32) * kKC + pos * 8);
-    return f.v;
-  };
-
-  u32x4_t wb[2][2][8];  // [ring slot][32-row block][k step]
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) wb[0][b][t] = wload(cb, b, t);
-  hdma(sH0, cb);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __builtin_amdgcn_s_barrier();
-
-  f32x16_t acc[2][MT / 32];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int mb = 0; mb < MT / 32; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[b][mb][i] = 0.f;
-
-  // One chunk on stage U (a compile-time constant: each stage stays one
-  // known LDS object in every instruction).  Chunk c + 1 goes into the other
-  // stage and ring slot first (both last read in chunk c - 1, before the
-  // last barrier; past the end, the last chunk again), so that any wait the
-  // compiler places before this chunk's stage reads comes before those
-  // loads; the chunk ends waiting for all of them, a chunk of products
-  // after they were issued.
-  auto chunk = [&](int c, auto stage_tag) {
-    constexpr int U = decltype(stage_tag)::value;
-    const bf16_t* sh = U ? sH1 : sH0;
-    const int cn = cb + min(c + 1, nkl - 1);
-    hdma(U ? sH0 : sH1, cn);
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) wb[U ^ 1][b][t] = wload(cn, b, t);
-    __builtin_amdgcn_sched_barrier(0);  // the loads stay ahead of the products
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      bf16x8_t hf[MT / 32];
-#pragma unroll
-      for (int mb = 0; mb < MT / 32; ++mb) hf[mb] = frag(sh, mb, t);
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        Frag8 wf;
-        wf.q = wb[U][b][t];
-#pragma unroll
-        for (int mb = 0; mb < MT / 32; ++mb) acc[b][mb] = mfma32(wf.v, hf[mb], acc[b][mb]);
-      }
-    }
-    // chunk c + 1 is in this wavefront's registers and stage rows; after
-    // the barrier, in everyone's
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __builtin_amdgcn_s_barrier();
-  };
-  for (int c0 = 0; c0 < nkl; c0 += 2) {
-    chunk(c0, std::integral_constant<int, 0>{});
-    chunk(c0 + 1, std::integral_constant<int, 1>{});
   }
   epilogue<MODE, MT>(acc, tl, s_key, keys, logits, part, M, V);
 }
@@ -640,13 +522,6 @@ void gemm8_store_kernel(const bf16_t* __restrict__ H, const bf16_t* __restrict__
                              0, 0, 0);
 }
 
-// The 256-row tile serves the LM head (one pass over k, argmax epilogue).
-// The split-K projections stay on 128-row tiles: with half as many tiles
-// they would take twice the splits, each with half the k range and twice
-// the partial sums, and measured slower (a 36-layer pass at 512 rows: 13.4
-// against 11.2 ms of projections).
-bool use_wide(int M) { return M >= kWideRows; }
-
 // The eight-wavefront LM head from this many rows on, and its W tiles.  One
 // workgroup fits a CU, so a launch runs in rounds of 256 workgroups, and a
 // round costs what its longest workgroup costs.  The vocabulary is split
@@ -762,17 +637,11 @@ hipError_t launch_gemm32_argmax(const void* hidden, const void* w_packed,
     }
     return hipGetLastError();
   }
-  const int rows = use_wide(M) ? 256 : 128;
-  const int nmt = (M + rows - 1) / rows;
+  const int nmt = (M + 127) / 128;
   const int total = nmt * gemm32_vtiles(V);
-  const bf16_t* h = static_cast<const bf16_t*>(hidden);
-  const bf16_t* w = static_cast<const bf16_t*>(w_packed);
-  if (use_wide(M))
-    hipLaunchKernelGGL(gemm32w_kernel<kGemmArgmax>, dim3(total), dim3(kThreads), 0, stream, h,
-                       w, keys, logits, nullptr, M, K, V, nmt, 1, total);
-  else
-    hipLaunchKernelGGL(gemm32_kernel<kGemmArgmax>, dim3(total), dim3(kThreads), 0, stream, h, w,
-                       keys, logits, nullptr, M, K, V, nmt, 1, total);
+  hipLaunchKernelGGL(gemm32_kernel<kGemmArgmax>, dim3(total), dim3(kThreads), 0, stream,
+                     static_cast<const bf16_t*>(hidden), static_cast<const bf16_t*>(w_packed), keys,
+                     logits, nullptr, M, K, V, nmt, 1, total);
   return hipGetLastError();
 }
 
