@@ -62,6 +62,11 @@ MODELS = {
     # in its own epilogue, as at Qwen3-8B scale
     "wide_mlp": ModelConfig("wide_mlp", layers=2, hidden=256, Hq=2, Hkv=1, D=128, inter=8192,
                             V=1000, seed=2005),
+    # one Qwen3-8B-shaped layer with a small vocabulary: the projections at
+    # their full widths (QKV 6144, O 4096, gate/up 24576, down 4096 over
+    # k = 12288), which from 256 rows run split-K on both W tile widths
+    "qwen3_8b_layer": ModelConfig("qwen3_8b_layer", layers=1, hidden=4096, Hq=32, Hkv=8, D=128,
+                                  inter=12288, V=3000, seed=2006),
 }
 
 
@@ -83,6 +88,11 @@ def _model_cases():
                                                             L_hi=120, seed=64)),
         "small_d128_B10_N64_M640": ("small_d128", r8.replace(B=10, Hq=8, Hkv=2, N=64, L_lo=10,
                                                              L_hi=90, seed=65)),
+        # one full-width Qwen3-8B layer at 512 rows (8 ragged sequences of 64
+        # nodes): gate/up on 384-row W tiles in 2 splits, the others on 256-row
+        # tiles in 4 or 8
+        "qwen3_8b_layer_B8_N64_M512": ("qwen3_8b_layer", r8.replace(B=8, N=64, L_lo=16, L_hi=200,
+                                                                    seed=66)),
         # the full Qwen3-8B-shaped stack on one 64-node tree over 1024 tokens
         "qwen3_8b_L1024_N64": ("qwen3_8b", q8),
     }
