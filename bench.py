@@ -128,7 +128,9 @@ def lmhead_kernel_name(M, V, dtype):
         return "lmhead_stream_kernel (packed W)"
     if M >= 256:
         n384, n256 = gemm8_plan(M, V)
-        names = (["gemm8_argmax_kernel<384>"] if n384 else []) + (["gemm8_argmax_kernel<256>"] if n256 else [])
+        nt = "true" if M <= 256 else "false"  # one H slice: non-temporal W loads
+        names = ([f"gemm8_argmax_kernel<384, {nt}>"] if n384 else []) + \
+            ([f"gemm8_argmax_kernel<256, {nt}>"] if n256 else [])
         return " + ".join(names + ["argmax_reduce_kernel"])
     return "gemm32_kernel + argmax_reduce_kernel"
 

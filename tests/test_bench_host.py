@@ -71,11 +71,12 @@ def test_algorithmic_work_of_the_default_workload():
 def test_lmhead_kernel_label_follows_the_library_choice():
     """The labels the profiles show for each workload's LM head."""
     b = _bench()
-    both = "gemm8_argmax_kernel<384> + gemm8_argmax_kernel<256> + argmax_reduce_kernel"
-    assert b.lmhead_kernel_name(4096, 151936, "bf16") == "gemm8_argmax_kernel<384> + argmax_reduce_kernel"
-    assert b.lmhead_kernel_name(512, 151936, "bf16") == both
-    assert b.lmhead_kernel_name(256, 151936, "bf16") == both
-    assert b.lmhead_kernel_name(256, 4163, "bf16") == "gemm8_argmax_kernel<256> + argmax_reduce_kernel"
+    both = "gemm8_argmax_kernel<384, {0}> + gemm8_argmax_kernel<256, {0}> + argmax_reduce_kernel"
+    assert b.lmhead_kernel_name(4096, 151936, "bf16") == \
+        "gemm8_argmax_kernel<384, false> + argmax_reduce_kernel"
+    assert b.lmhead_kernel_name(512, 151936, "bf16") == both.format("false")
+    assert b.lmhead_kernel_name(256, 151936, "bf16") == both.format("true")
+    assert b.lmhead_kernel_name(256, 4163, "bf16") == "gemm8_argmax_kernel<256, true> + argmax_reduce_kernel"
     assert b.lmhead_kernel_name(64, 151936, "bf16") == "lmhead_stream_kernel (packed W)"
     assert b.lmhead_kernel_name(7, 1000, "f32") == "lmhead_f32_kernel"
 
