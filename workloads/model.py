@@ -82,6 +82,10 @@ def _model_cases():
                                                             L_hi=200, seed=62)),
         # unsplit gate/up projection with the fused silu(gate) * up epilogue
         "wide_mlp_N64_L200": ("wide_mlp", q8.replace(Hq=2, Hkv=1, L_lo=200, L_hi=200, seed=63)),
+        # 256 rows: one H slice (the LM head's non-temporal W loads, the
+        # projections' splits with no slice group)
+        "small_d128_B4_N64_M256": ("small_d128", r8.replace(B=4, Hq=8, Hkv=2, N=64, L_lo=10,
+                                                            L_hi=150, seed=67)),
         # 512 and 640 rows: the products with 256-row H tiles (the last slice
         # of 640 rows half empty)
         "small_d128_B8_N64_M512": ("small_d128", r8.replace(B=8, Hq=8, Hkv=2, N=64, L_lo=10,
