@@ -742,17 +742,42 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     pstride = 1;
     prow0 = (((size_t)b * a.Hkv + g) * ((size_t)a.nqblk * a.rows) + row) * a.nsplit;
   }
+  // up to kRegSplits splits: every load issued before the first use, the
+  // same arithmetic in the same order as the general loop below
+  constexpr int kRegSplits = 8;
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[(prow0 + s * pstride) * 2]);
-  const float m_use = (mx == -INFINITY) ? 0.f : mx;
   float lsum = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
-    const size_t pr = prow0 + s * pstride;
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - m_use);
-    lsum += w * a.part_ml[pr * 2 + 1];
-    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + pr * D + d4 * 4);
-    acc += w * v;
+  if (ns <= kRegSplits) {
+    float2 ml[kRegSplits];
+    f32x4_t vo[kRegSplits];
+#pragma unroll
+    for (int s = 0; s < kRegSplits; ++s) {
+      const size_t pr = prow0 + (size_t)(s < ns ? s : 0) * pstride;
+      ml[s] = *reinterpret_cast<const float2*>(a.part_ml + pr * 2);
+      vo[s] = *reinterpret_cast<const f32x4_t*>(a.part_o + pr * D + d4 * 4);
+    }
+#pragma unroll
+    for (int s = 0; s < kRegSplits; ++s)
+      if (s < ns) mx = fmaxf(mx, ml[s].x);
+    const float m_use = (mx == -INFINITY) ? 0.f : mx;
+#pragma unroll
+    for (int s = 0; s < kRegSplits; ++s)
+      if (s < ns) {
+        const float w = __builtin_amdgcn_exp2f(ml[s].x - m_use);
+        lsum += w * ml[s].y;
+        acc += w * vo[s];
+      }
+  } else {
+    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[(prow0 + s * pstride) * 2]);
+    const float m_use = (mx == -INFINITY) ? 0.f : mx;
+    for (int s = 0; s < ns; ++s) {
+      const size_t pr = prow0 + s * pstride;
+      const float w = __builtin_amdgcn_exp2f(a.part_ml[pr * 2] - m_use);
+      lsum += w * a.part_ml[pr * 2 + 1];
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + pr * D + d4 * 4);
+      acc += w * v;
+    }
   }
   const float inv = 1.f / lsum;
   const int node = row / a.G;
