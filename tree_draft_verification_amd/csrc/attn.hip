@@ -561,6 +561,34 @@ void attn_bf16_kernel(AttnArgs a) {
     //   V: piece x at position x ^ 2 (r & 3): the transposing reads (4 rows
     //      x 4 eight-byte units per 16 lanes) touch 32 distinct banks.
     auto tdma = [&](bf16_t* kbuf, bf16_t* vbuf, int krow0, int nvalid, bool tree) {
+      if constexpr (PAGED) {
+        if (!tree && nvalid == kKT && sh >= 4) {
+          // a whole prefix tile (krow0 a multiple of 64): each wavefront's 16
+          // rows lie in one page of at least 16 rows, one entry per wavefront
+          const int r0 = (kKT / NW) * wave;
+          int pg = bt[(krow0 + r0) >> sh];
+          if ((unsigned)pg >= (unsigned)a.num_pages) {
+            bad_page = 1;
+            pg = 0;
+          }
+          const size_t pbase = (((size_t)pg * a.Hkv + g) << sh) * D;
+#pragma unroll
+          for (int i = 0; i < kKT / (4 * NW); ++i) {
+            const int r = r0 + 4 * i + (lane >> 4);
+            const size_t ro = pbase + (size_t)((krow0 + r) & ((1 << sh) - 1)) * D;
+            const int xk = (lane & 15) ^ (r & 15);
+            const int xv = (lane & 15) ^ (2 * (r & 3));
+            const int dst = ((kKT / NW) * wave + 4 * i) * D;
+            __builtin_amdgcn_global_load_lds((const void*)(a.k + ro + xk * 8),
+                                             (__attribute__((address_space(3))) void*)(kbuf + dst),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(a.v + ro + xv * 8),
+                                             (__attribute__((address_space(3))) void*)(vbuf + dst),
+                                             16, 0, 0);
+          }
+          return;
+        }
+      }
       const int last = krow0 + nvalid - 1;
 #pragma unroll
       for (int i = 0; i < kKT / (4 * NW); ++i) {
