@@ -322,7 +322,9 @@ void attn_bf16_kernel(AttnArgs a) {
   // ---- where key/value rows live: one contiguous plane per (sequence, KV
   // head), or pages of a pool named by the block table.  For pages, the lanes
   // that load a row look up its page entry themselves (a 4-byte load; a
-  // sequence's entries are read by all its query blocks, so they sit in L2):
+  // sequence's entries are read by all its query blocks, so they sit in L2;
+  // a whole prefix tile with pages of 16 rows or more takes one entry per
+  // wavefront):
   // no entries are staged in LDS, so neither the page size nor the length of
   // a split is bounded by LDS.  An entry outside the pool reads page 0 and
   // flags TV_STATUS_BAD_PAGE at the end.
