@@ -232,6 +232,9 @@ def main():
     ap.add_argument("--compact-path-depth", type=int, default=20,
                     help="accepted paths of this depth through level-ordered trees of width 7 "
                          "(0: the deepest root paths of the workload's own trees)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="also time the LM head's plain product through torch.matmul (the "
+                         "vendor GEMM library, no argmax) for comparison")
     ap.add_argument("--calibrate-copy", type=int, default=0,
                     help="only run a plain device copy of this many bytes")
     args = ap.parse_args()
@@ -400,6 +403,22 @@ def main():
     torch.cuda.synchronize()
     lm_rowmajor_us = rm_ev[0].elapsed_time(rm_ev[1]) * 1e3 / rm_reps
 
+    # For comparison only: the same product through the vendor GEMM library
+    # (logits written in bf16, no argmax), after the step's own timing.
+    lib_us = None
+    if args.library_gemm and wl.dtype == "bf16":
+        wt = w.t()
+        for _ in range(3):
+            lib_out = torch.matmul(hid, wt)
+        torch.cuda.synchronize()
+        rm_ev[0].record()
+        for _ in range(rm_reps):
+            lib_out = torch.matmul(hid, wt)
+        rm_ev[1].record()
+        torch.cuda.synchronize()
+        lib_us = rm_ev[0].elapsed_time(rm_ev[1]) * 1e3 / rm_reps
+        del lib_out
+
     names = ["attn", "lmhead", "accept", "compact"]
     per = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
            * 1e3 for j, n in enumerate(names)}
@@ -457,6 +476,8 @@ def main():
         "kernels": kernels,
         "lmhead_rowmajor_us": round(lm_rowmajor_us, 2),
     }
+    if lib_us is not None:
+        res["library_gemm_us"] = round(lib_us, 2)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, a, lm, coins)
     print(json.dumps(res), flush=True)
