@@ -394,14 +394,13 @@ __device__ __forceinline__ void gemm8_body(const bf16_t* __restrict__ H,
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __builtin_amdgcn_s_barrier();
   // chunk c on stage U (compile-time: each stage one known LDS object); the
-  // loads of chunk c + 1 into the other stage go first, the chunk ends
-  // waiting for them
+  // loads of chunk c + 1 into the other stage are issued among its products,
+  // and the chunk ends waiting for them
   auto chunk = [&](int c, auto stage_tag) {
     constexpr int U = decltype(stage_tag)::value;
     const bf16_t* sw = U ? sW1 : sW0;
     const bf16_t* sh = U ? sH1 : sH0;
     dma(U ? sW0 : sW1, U ? sH0 : sH1, min(c + 1, cb + nkl - 1));
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < KC / 16; ++t) {
       bf16x8_t wf[BW], hf[BH];
@@ -413,6 +412,17 @@ __device__ __forceinline__ void gemm8_body(const bf16_t* __restrict__ H,
       for (int i = 0; i < BW; ++i)
 #pragma unroll
         for (int j = 0; j < BH; ++j) acc[i][j] = mfma32(wf[i], hf[j], acc[i][j]);
+    }
+    // Schedule: one product, then each of the wavefront's copies for the
+    // next chunk followed by four products.  Issued all at once ahead of the
+    // products, the copies stalled the wavefront at issue while the memory
+    // path drained them, and its products started late (7 % on the
+    // 4096 x 2048 x 151936 product; 3 or 5 products per copy measured slower).
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // matrix instruction
+#pragma unroll
+    for (int k = 0; k < DMA_W + DMA_H; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // vector memory (a copy)
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_s_barrier();
