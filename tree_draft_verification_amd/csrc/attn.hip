@@ -470,6 +470,20 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int qb = 0; qb < QBW; ++qb) s[qb][kb] = mfma16x16x32(kf[kb][ks].v, qf[qb][ks], s[qb][kb]);
+    if constexpr (kDma) {
+      // The next tile's copies (issued just before, in this basic block) go
+      // out among these products, one per QBW products after the K fragment
+      // reads, instead of all ahead of them, where the wavefront waited at
+      // issue while the memory path drained them (2-3 % on the long-prefix
+      // workloads; one per 2 QBW products gained less).
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * DS, 0);  // LDS reads: K fragments
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // matrix instruction
+#pragma unroll
+      for (int k = 0; k < 2 * kKT / (4 * NW); ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // vector memory (a copy)
+        __builtin_amdgcn_sched_group_barrier(0x008, QBW, 0);
+      }
+    }
     // O^T += V^T P^T below reads these (the first half of the output rows'
     // fragments are in flight during the softmax, the second half during the
     // first half's products); k-slot e of lane group kg is key 32u + 4kg + e
@@ -613,12 +627,14 @@ void attn_bf16_kernel(AttnArgs a) {
       const bf16_t* vb_lds = U ? sV1 : sV0;
       int krow0, nvalid, tt;
       tile_rows(it, krow0, nvalid, tt);
-      if (it + 1 < n_tiles) {
+      {
+        // the next tile's copies; the last tile copies itself again into the
+        // free buffers (never read: an L2 hit), so that the copies share a
+        // basic block with the products they are spread among
         int k1r, n1, t1;
-        tile_rows(it + 1, k1r, n1, t1);
+        tile_rows(min(it + 1, n_tiles - 1), k1r, n1, t1);
         tdma(U ? sK0 : sK1, U ? sV0 : sV1, k1r, n1, t1 >= 0);
       }
-      __builtin_amdgcn_sched_barrier(0);  // the next tile's loads go out first
       // V^T operand rows d = db*16 + l16 for keys key0 .. key0+3: lane j of
       // a 16-lane group points at key key0 + j/4, dims db*16 + 4 (j % 4) ..
       // + 3, and the transposing read hands lane j dim db*16 + j of the four
